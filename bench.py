@@ -1,0 +1,287 @@
+"""Benchmark of the mHC hot path on one MI355X.
+
+A step is one pass of the whole hot path over one batch: hc_pre forward,
+hc_post forward, hc_post backward and hc_pre backward (with recompute), all
+through the C ABI, on the long-sequence workload B=1, S=4096 tokens, N=4
+streams, D=5120, bf16 storage of x / y / h / x_next / gradients and fp32 math.
+Inputs are seeded synthetic tensors already resident in HBM; two input sets
+alternate between steps so that no step finds its inputs in the 256 MB
+Infinity Cache left warm by the previous one.
+
+Prints one JSON line.  `value` is tokens/s of the full step; the forward pair
+(hc_pre + hc_post, the HBM-roofline headline) is reported in "forward";
+"roofline" describes the kernel that takes the most time in the step, timed
+with HIP events on its own stream; "cpu_baseline" times the fp64 oracle on the
+host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
+METRIC = "mHC pre+post tokens/s and HBM GB/s (% of peak) at S=4096,N=4,D=5120"
+
+WORKLOADS = {
+    # name: (T, N, D, io)
+    "pro_s4096_bf16": (4096, 4, 5120, "bf16"),
+    "pro_s1024_f32": (1024, 4, 5120, "f32"),
+    "flash_s2048_f32": (2048, 4, 2560, "f32"),
+}
+
+
+def algo_bytes(T, N, D, io):
+    """Algorithmic HBM bytes per call: every tensor read or written once, the
+    fp32 coefficients counted, φ (and dφ) counted once per call."""
+    e = 2 if io == "bf16" else 4
+    K, C = N * D, N * N + 2 * N
+    coef = (N + N * N) * 4  # H_post + H_res (or their gradients), fp32
+    phi = K * C * 4 + C * 4
+    return {
+        "mhc_pre": T * (K * e + D * e + C * 4) + phi,
+        "mhc_post": T * (K * e + D * e + coef + K * e),
+        "mhc_post_bwd": T * (3 * K * e + 2 * D * e + 2 * coef),
+        "mhc_pre_bwd": T * (D * e + 3 * K * e + coef) + 2 * phi,
+    }
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "residual_stream_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_call, src_hash):
+    """HBM traffic per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            doc = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = doc.get(kernel_call)
+    if not ent or ent.get("source_hash") != src_hash:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(T, N, D, io, seed):
+    """Time the fp64 oracle (as it stands) on the host: full forward + backward
+    over the whole batch, on every core BLAS uses."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import mhc_oracle as O
+    from residual_stream_amd.inputs import make_inputs
+
+    inp = make_inputs(T, N, D, io=io, seed=seed, grads=True)
+    t0 = time.perf_counter()
+    pre = O.hc_pre(inp.x, inp.phi, inp.bias, inp.alphas, inp.eps, inp.iters)
+    O.hc_post(inp.x, inp.y, pre["H_post"], pre["H_res"])
+    dx, dy, dHp, dHr = O.hc_post_bwd(inp.dx_next, inp.x, inp.y, pre["H_post"], pre["H_res"])
+    O.hc_pre_bwd(inp.dh, inp.x, inp.phi, inp.bias, dHp, dHr, inp.alphas, inp.eps, inp.iters)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    del inp, pre, dx, dy
+    return {"value": T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"full forward+backward of the {T}-token batch (N={N}, D={D}, {io} inputs "
+                      f"upcast to fp64), one run, {dt:.2f} s; matmuls on {threads} BLAS threads, "
+                      f"einsum/elementwise parts single-threaded; "
+                      f"{len(os.sched_getaffinity(0))} host cores available"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="pro_s4096_bf16", choices=sorted(WORKLOADS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the mHC hot path is token-local and this "
+              "build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from residual_stream_amd import mhc
+    from residual_stream_amd.inputs import make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mhc.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    T, N, D, io = WORKLOADS[args.workload]
+    K, C = N * D, N * N + 2 * N
+    tdt = torch.bfloat16 if io == "bf16" else torch.float32
+    kw = dict(iters=20, eps=1e-6, alphas=(0.01, 0.01, 0.01))
+
+    # Two input sets (different seeds), resident in HBM; outputs preallocated.
+    sets = []
+    for s in range(2):
+        inp = make_inputs(T, N, D, io=io, seed=args.seed + s, grads=True)
+
+        def t(a, dt=None):
+            x = torch.from_numpy(a)
+            return (x.to(dt) if dt is not None else x).to(dev)
+
+        st = {"x": t(inp.x, tdt), "y": t(inp.y, tdt), "phi": t(inp.phi), "bias": t(inp.bias),
+              "dh": t(inp.dh, tdt), "dxn": t(inp.dx_next, tdt)}
+        st["h"] = torch.empty((T, D), dtype=tdt, device=dev)
+        st["Hp"] = torch.empty((T, N), dtype=torch.float32, device=dev)
+        st["Hq"] = torch.empty((T, N), dtype=torch.float32, device=dev)
+        st["Hr"] = torch.empty((T, N, N), dtype=torch.float32, device=dev)
+        st["xn"] = torch.empty((T, N, D), dtype=tdt, device=dev)
+        st["dx"] = torch.empty((T, N, D), dtype=tdt, device=dev)
+        st["dy"] = torch.empty((T, D), dtype=tdt, device=dev)
+        st["dHp"] = torch.empty((T, N), dtype=torch.float32, device=dev)
+        st["dHr"] = torch.empty((T, N, N), dtype=torch.float32, device=dev)
+        st["dphi"] = torch.empty((K, C), dtype=torch.float32, device=dev)
+        st["dbias"] = torch.empty((C,), dtype=torch.float32, device=dev)
+        st["dalpha"] = torch.empty((4,), dtype=torch.float32, device=dev)
+        sets.append(st)
+        del inp
+    ws_pre = mhc.workspace_bytes("pre", T, N, D, mhc.MHC_BF16 if io == "bf16" else mhc.MHC_F32)
+    ws_bwd = mhc.workspace_bytes("pre_bwd", T, N, D, mhc.MHC_BF16 if io == "bf16" else mhc.MHC_F32)
+    ws_pre_t = torch.empty(max(ws_pre, 256), dtype=torch.uint8, device=dev) if ws_pre else None
+    ws_bwd_t = torch.empty(ws_bwd, dtype=torch.uint8, device=dev)
+
+    stream = torch.cuda.current_stream()
+
+    def call_pre(st):
+        mhc.mhc_pre(st["x"], st["phi"], st["bias"], out=(st["h"], st["Hp"], st["Hq"], st["Hr"]),
+                    workspace=ws_pre_t, stream=stream, **kw)
+
+    def call_post(st):
+        mhc.mhc_post(st["x"], st["y"], st["Hq"], st["Hr"], out=st["xn"], stream=stream)
+
+    def call_post_bwd(st):
+        mhc.mhc_post_bwd(st["dxn"], st["x"], st["y"], st["Hq"], st["Hr"],
+                         out=(st["dx"], st["dy"], st["dHp"], st["dHr"]), stream=stream)
+
+    def call_pre_bwd(st):
+        mhc.mhc_pre_bwd(st["dh"], st["x"], st["phi"], st["bias"], st["dHp"], st["dHr"], st["dx"],
+                        out=(st["dphi"], st["dbias"], st["dalpha"]), workspace=ws_bwd_t,
+                        stream=stream, **kw)
+
+    calls = [("mhc_pre", call_pre), ("mhc_post", call_post), ("mhc_post_bwd", call_post_bwd),
+             ("mhc_pre_bwd", call_pre_bwd)]
+
+    def step(i):
+        st = sets[i % 2]
+        for _, f in calls:
+            f(st)
+
+    print(f"[bench] workload {args.workload}: T={T} N={N} D={D} io={io}; warmup {args.warmup}",
+          file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K full steps ----
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    print(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
+
+    # ---- per-call HIP-event timing (same stream), inputs alternating ----
+    ab = algo_bytes(T, N, D, io)
+    per_call = {}
+    for name, f in calls:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for i in range(args.steps):
+            st = sets[i % 2]
+            # keep the dependency order of a real step: the call's inputs exist
+            evs[i][0].record(stream)
+            f(st)
+            evs[i][1].record(stream)
+            # the other calls of the step run untimed between timed launches
+            for n2, f2 in calls:
+                if n2 != name:
+                    f2(sets[(i + 1) % 2])
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in evs)
+        avg = sum(ts) / len(ts)
+        per_call[name] = {"avg_us": avg * 1e3, "median_us": ts[len(ts) // 2] * 1e3,
+                          "algo_bytes": ab[name], "gbps": ab[name] / (avg * 1e-3) / 1e9}
+
+    # forward pair alone (hc_pre + hc_post), the HBM-roofline headline
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        st = sets[i % 2]
+        evs[i][0].record(stream)
+        call_pre(st)
+        call_post(st)
+        evs[i][1].record(stream)
+        call_post_bwd(sets[(i + 1) % 2])
+        call_pre_bwd(sets[(i + 1) % 2])
+    torch.cuda.synchronize()
+    fwd_ts = sorted(a.elapsed_time(b) for a, b in evs)
+    fwd_ms = sum(fwd_ts) / len(fwd_ts)
+    fwd_bytes = ab["mhc_pre"] + ab["mhc_post"]
+
+    dom = max(per_call, key=lambda k: per_call[k]["avg_us"])
+    src_hash = kernel_source_hash()
+    traffic = load_traffic(dom, src_hash)
+    achieved = per_call[dom]["gbps"]
+    step_bytes = sum(ab.values())
+
+    out = {
+        "metric": METRIC,
+        "value": T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": io,
+        "data": "synthetic (seeded Gaussian x, y, dh, dx_next; phi ~ N(0, 1/(N*D)); bias ~ N(0, 0.1))",
+        "config": {"workload": f"{args.workload}_fwd_bwd", "T": T, "N": N, "D": D, "io": io,
+                   "sinkhorn_iters": 20, "alpha": 0.01,
+                   "step": "mhc_pre + mhc_post + mhc_post_bwd + mhc_pre_bwd"},
+        "step_algo_bytes": step_bytes,
+        "step_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
+        "forward": {"calls": "mhc_pre + mhc_post", "avg_us": fwd_ms * 1e3,
+                    "tokens_per_s": T / (fwd_ms * 1e-3), "algo_bytes": fwd_bytes,
+                    "gbps": fwd_bytes / (fwd_ms * 1e-3) / 1e9,
+                    "frac_of_peak": fwd_bytes / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+        "per_call": per_call,
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
+        "kernel_source_hash": src_hash,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(T, N, D, io, args.seed)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,132 @@
+/*
+ * mhc.h — C ABI of the MI355X (gfx950) mHC hot path: hc_pre / hc_post and
+ * their backward.
+ *
+ * What the calls compute (cited by page title and section):
+ *
+ *   hc_pre   — openPangu 2.0 analysis, §5.3 "mHC" formula block: per token,
+ *              x̄ = RMSNorm(x) over the flattened N·D state, logits
+ *              ℓ = α_g·(x̄·φ) + b with columns [pre N | post N | res N²],
+ *              H_pre = sigmoid(ℓ_pre), H_post = 2·sigmoid(ℓ_post),
+ *              H_res = Sinkhorn(exp(reshape(ℓ_res, N, N))) (row-normalise then
+ *              column-normalise, `sinkhorn_iters` rounds; 20 in the model table),
+ *              and the collapsed sublayer input h = Σ_n H_pre[n]·x[n].
+ *   hc_post  — same section (roles of the maps) and the Ascend mHC Triton
+ *              article's definition paragraph: x_next[n] = Σ_m H_res[n,m]·x[m]
+ *              + H_post[n]·y.
+ *   backward — the exact derivative of the above; hc_pre's backward recomputes
+ *              norm, logits and Sinkhorn from x (the Ascend article's
+ *              intra-layer recompute paragraph keeps only the hc_pre input and
+ *              the sublayer outputs).
+ *
+ * Conventions for every call:
+ *   - Tensors are device pointers (hipMalloc'd or equivalent), row-major and
+ *     contiguous, owned by the caller.  x, y, h, x_next, dh, dx_next, dx, dy
+ *     use the I/O dtype `desc->io` (fp32, or bf16 stored as raw 16-bit
+ *     words); φ, bias, H_*, dH_*, dφ, dbias, dα are always fp32.
+ *   - Layouts: x[T][N][D], y[T][D], h[T][D], x_next[T][N][D], φ[N·D][C] with
+ *     C = N²+2N, bias[C], H_pre[T][N], H_post[T][N], H_res[T][N][N] (row =
+ *     destination stream).
+ *   - Alignment: every pointer 16-byte aligned.
+ *   - Work is enqueued on `stream` and runs asynchronously; the library never
+ *     allocates, frees or synchronises, and keeps no global state (calls are
+ *     thread-safe).  Outputs are overwritten, except `dx` of mhc_pre_bwd,
+ *     which is read-modify-write.
+ *   - Errors: argument checks are synchronous and return a status without
+ *     launching anything.  A failed launch returns MHC_ERR_HIP.  Device faults
+ *     surface at the caller's next synchronisation, as in HIP.
+ *   - Aliasing: outputs must not alias inputs (x_next ≠ x, y; dx ≠ dx_next).
+ *   - Results are bitwise reproducible for the same inputs, shape and device
+ *     (no atomics; reductions have a fixed order).
+ */
+#ifndef MHC_H
+#define MHC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MHC_ABI_VERSION 1
+
+typedef enum mhc_dtype { MHC_F32 = 0, MHC_BF16 = 1 } mhc_dtype;
+
+typedef enum mhc_status {
+  MHC_OK = 0,
+  MHC_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, workspace too small */
+  MHC_ERR_UNSUPPORTED = 2, /* N not in {1,2,4,8}, D not a multiple of 8, too many rounds */
+  MHC_ERR_HIP = 3          /* the HIP runtime rejected a launch */
+} mhc_status;
+
+/* Problem descriptor.  T = tokens (batch × sequence), N streams, D hidden size
+ * (multiple of 8), io = mhc_dtype, sinkhorn_iters ≥ 1 (≤ 64 for mhc_pre_bwd),
+ * eps ≥ 0 inside the RMS square root, alpha_* the per-group gate scalars
+ * multiplying the normalised projection before the bias is added. */
+typedef struct mhc_desc {
+  int64_t T;
+  int32_t N;
+  int32_t D;
+  int32_t io;
+  int32_t sinkhorn_iters;
+  float eps;
+  float alpha_pre;
+  float alpha_post;
+  float alpha_res;
+} mhc_desc;
+
+/* Bytes of device workspace mhc_pre needs (0 if none).  Never fails; returns 0
+ * for an invalid descriptor. */
+size_t mhc_pre_workspace_bytes(const mhc_desc* desc);
+
+/* hc_pre forward.  Reads x once per token tile, writes h[T][D] (I/O dtype) and
+ * the fp32 coefficients H_pre, H_post, H_res.  `workspace` (may be NULL when
+ * mhc_pre_workspace_bytes is 0) is scratch owned by the caller, at least
+ * that many bytes, 256-byte aligned; its contents on entry are ignored. */
+mhc_status mhc_pre(const mhc_desc* desc, const void* x, const float* phi, const float* bias,
+                   void* h, float* H_pre, float* H_post, float* H_res,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* hc_post forward: x_next = H_res·x + H_post ⊗ y (single read of x and y, single
+ * write of x_next). */
+mhc_status mhc_post(const mhc_desc* desc, const void* x, const void* y, const float* H_post,
+                    const float* H_res, void* x_next, hipStream_t stream);
+
+/* hc_post backward.  Given dx_next, writes
+ *   dx[m]       = Σ_n H_res[n,m]·dx_next[n]        (I/O dtype, overwritten)
+ *   dy          = Σ_n H_post[n]·dx_next[n]         (I/O dtype)
+ *   dH_post[n]  = <dx_next[n], y>,  dH_res[n,m] = <dx_next[n], x[m]>   (fp32)
+ * Must run before mhc_pre_bwd, which adds hc_pre's contribution into dx. */
+mhc_status mhc_post_bwd(const mhc_desc* desc, const void* dx_next, const void* x, const void* y,
+                        const float* H_post, const float* H_res, void* dx, void* dy,
+                        float* dH_post, float* dH_res, hipStream_t stream);
+
+/* Bytes of device workspace mhc_pre_bwd needs; 0 for an invalid descriptor. */
+size_t mhc_pre_bwd_workspace_bytes(const mhc_desc* desc);
+
+/* hc_pre backward with recompute from x.  Inputs: dh[T][D] (gradient of h),
+ * x, φ, bias, and dH_post / dH_res from mhc_post_bwd.  Outputs:
+ *   dx (in/out, I/O dtype): on entry hc_post's contribution, on exit the total;
+ *   dphi[N·D][C], dbias[C] (fp32, overwritten);
+ *   dalpha[3] (fp32: d/dα_pre, d/dα_post, d/dα_res) or NULL to skip.
+ * `workspace` must hold mhc_pre_bwd_workspace_bytes(desc) bytes, 256-byte
+ * aligned; its contents on entry are ignored. */
+mhc_status mhc_pre_bwd(const mhc_desc* desc, const void* dh, const void* x, const float* phi,
+                       const float* bias, const float* dH_post, const float* dH_res, void* dx,
+                       float* dphi, float* dbias, float* dalpha, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* mhc_status_string(mhc_status status);
+
+/* MHC_ABI_VERSION of the built library. */
+int mhc_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHC_H */

@@ -1,0 +1,59 @@
+// hc_post forward: x_next[n] = Σ_m H_res[n,m]·x[m] + H_post[n]·y
+// (openPangu 2.0 analysis, §5.3 roles of the maps; Ascend mHC Triton article,
+// definition paragraph).  Pure stream: x and y read once, x_next written once.
+#include "mhc_device.h"
+#include "mhc_internal.h"
+
+namespace mhc {
+
+constexpr int kPostThreads = 256;
+
+// One workgroup per token; each thread owns 8 consecutive d of every stream.
+template <int N, int IO>
+__global__ __launch_bounds__(kPostThreads) void hc_post_generic(
+    const void* __restrict__ x, const void* __restrict__ y, const float* __restrict__ H_post,
+    const float* __restrict__ H_res, void* __restrict__ x_next, int D) {
+  const int64_t t = blockIdx.x;
+  float hr[N][N], hp[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    hp[n] = H_post[t * N + n];
+#pragma unroll
+    for (int m = 0; m < N; ++m) hr[n][m] = H_res[(t * N + n) * N + m];
+  }
+  const int64_t xb = t * (int64_t)N * D;
+  for (int d0 = threadIdx.x * 8; d0 < D; d0 += kPostThreads * 8) {
+    float xv[N][8], yv[8];
+    load8<IO>(y, t * D + d0, yv);
+#pragma unroll
+    for (int m = 0; m < N; ++m) load8<IO>(x, xb + (int64_t)m * D + d0, xv[m]);
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      float o[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float a = hp[n] * yv[j];
+#pragma unroll
+        for (int m = 0; m < N; ++m) a += hr[n][m] * xv[m][j];
+        o[j] = a;
+      }
+      store8<IO>(x_next, xb + (int64_t)n * D + d0, o);
+    }
+  }
+}
+
+hipError_t launch_post(const mhc_desc& d, const void* x, const void* y, const float* H_post,
+                       const float* H_res, void* x_next, hipStream_t s) {
+  bool ok = dispatch_n(d.N, [&](auto n_) {
+    dispatch_io(d.io, [&](auto io_) {
+      constexpr int N = decltype(n_)::value;
+      constexpr int IO = decltype(io_)::value;
+      hipLaunchKernelGGL((hc_post_generic<N, IO>), dim3((unsigned)d.T), dim3(kPostThreads), 0, s,
+                         x, y, H_post, H_res, x_next, d.D);
+    });
+  });
+  if (!ok) return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace mhc

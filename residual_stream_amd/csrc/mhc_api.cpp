@@ -1,0 +1,146 @@
+// C ABI of the mHC hot path (declared in include/mhc.h): argument validation
+// and dispatch to the gfx950 kernels.  No allocation, no synchronisation, no
+// global state.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cmath>
+#include <limits>
+
+#include "../../include/mhc.h"
+#include "mhc_internal.h"
+
+namespace {
+
+constexpr int kMaxIters = 100000;
+constexpr int kMaxBwdIters = 64;
+
+bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool finite(float v) { return std::isfinite(v); }
+
+// Shape and scalar checks common to every call.
+mhc_status check_desc(const mhc_desc* d) {
+  if (d == nullptr) return MHC_ERR_INVALID_ARG;
+  if (d->T < 1 || d->T > std::numeric_limits<int32_t>::max()) return MHC_ERR_INVALID_ARG;
+  if (d->io != MHC_F32 && d->io != MHC_BF16) return MHC_ERR_INVALID_ARG;
+  if (d->sinkhorn_iters < 1) return MHC_ERR_INVALID_ARG;
+  if (!finite(d->eps) || d->eps < 0.f) return MHC_ERR_INVALID_ARG;
+  if (!finite(d->alpha_pre) || !finite(d->alpha_post) || !finite(d->alpha_res))
+    return MHC_ERR_INVALID_ARG;
+  if (d->N != 1 && d->N != 2 && d->N != 4 && d->N != 8) return MHC_ERR_UNSUPPORTED;
+  if (d->D < 8 || d->D % 8 != 0 || d->D > (1 << 24)) return MHC_ERR_UNSUPPORTED;
+  if (d->sinkhorn_iters > kMaxIters) return MHC_ERR_UNSUPPORTED;
+  return MHC_OK;
+}
+
+size_t io_bytes(const mhc_desc* d) { return d->io == MHC_F32 ? 4 : 2; }
+
+// True if the byte ranges [a, a+na) and [b, b+nb) overlap.
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+bool workspace_ok(const void* ws, size_t have, size_t need) {
+  if (need == 0) return true;
+  if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return false;
+  return have >= need;
+}
+
+mhc_status from_hip(hipError_t e) { return e == hipSuccess ? MHC_OK : MHC_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int mhc_abi_version(void) { return MHC_ABI_VERSION; }
+
+const char* mhc_status_string(mhc_status s) {
+  switch (s) {
+    case MHC_OK: return "ok";
+    case MHC_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad size or scalar, workspace too small, aliasing)";
+    case MHC_ERR_UNSUPPORTED: return "unsupported shape (N must be 1, 2, 4 or 8; D a multiple of 8; iteration limit)";
+    case MHC_ERR_HIP: return "HIP runtime error while launching";
+  }
+  return "unknown status";
+}
+
+size_t mhc_pre_workspace_bytes(const mhc_desc* d) {
+  if (check_desc(d) != MHC_OK) return 0;
+  return mhc::pre_workspace_bytes(*d);
+}
+
+size_t mhc_pre_bwd_workspace_bytes(const mhc_desc* d) {
+  if (check_desc(d) != MHC_OK) return 0;
+  return mhc::pre_bwd_workspace_bytes(*d);
+}
+
+mhc_status mhc_pre(const mhc_desc* d, const void* x, const float* phi, const float* bias, void* h,
+                   float* H_pre, float* H_post, float* H_res, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+  mhc_status st = check_desc(d);
+  if (st != MHC_OK) return st;
+  if (!aligned16(x) || !aligned16(phi) || !aligned16(bias) || !aligned16(h) || !aligned16(H_pre) ||
+      !aligned16(H_post) || !aligned16(H_res))
+    return MHC_ERR_INVALID_ARG;
+  const size_t T = (size_t)d->T, N = (size_t)d->N, D = (size_t)d->D;
+  if (overlaps(h, T * D * io_bytes(d), x, T * N * D * io_bytes(d))) return MHC_ERR_INVALID_ARG;
+  if (!workspace_ok(workspace, workspace_bytes, mhc::pre_workspace_bytes(*d)))
+    return MHC_ERR_INVALID_ARG;
+  return from_hip(mhc::launch_pre(*d, x, phi, bias, h, H_pre, H_post, H_res, workspace, stream));
+}
+
+mhc_status mhc_post(const mhc_desc* d, const void* x, const void* y, const float* H_post,
+                    const float* H_res, void* x_next, hipStream_t stream) {
+  mhc_status st = check_desc(d);
+  if (st != MHC_OK) return st;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(H_post) || !aligned16(H_res) ||
+      !aligned16(x_next))
+    return MHC_ERR_INVALID_ARG;
+  const size_t b = io_bytes(d), T = (size_t)d->T, N = (size_t)d->N, D = (size_t)d->D;
+  if (overlaps(x_next, T * N * D * b, x, T * N * D * b) || overlaps(x_next, T * N * D * b, y, T * D * b))
+    return MHC_ERR_INVALID_ARG;
+  return from_hip(mhc::launch_post(*d, x, y, H_post, H_res, x_next, stream));
+}
+
+mhc_status mhc_post_bwd(const mhc_desc* d, const void* dx_next, const void* x, const void* y,
+                        const float* H_post, const float* H_res, void* dx, void* dy,
+                        float* dH_post, float* dH_res, hipStream_t stream) {
+  mhc_status st = check_desc(d);
+  if (st != MHC_OK) return st;
+  if (!aligned16(dx_next) || !aligned16(x) || !aligned16(y) || !aligned16(H_post) ||
+      !aligned16(H_res) || !aligned16(dx) || !aligned16(dy) || !aligned16(dH_post) ||
+      !aligned16(dH_res))
+    return MHC_ERR_INVALID_ARG;
+  const size_t b = io_bytes(d), T = (size_t)d->T, N = (size_t)d->N, D = (size_t)d->D;
+  const size_t big = T * N * D * b, small = T * D * b;
+  if (overlaps(dx, big, dx_next, big) || overlaps(dx, big, x, big) || overlaps(dx, big, y, small) ||
+      overlaps(dy, small, dx_next, big) || overlaps(dy, small, x, big) || overlaps(dy, small, dx, big))
+    return MHC_ERR_INVALID_ARG;
+  return from_hip(
+      mhc::launch_post_bwd(*d, dx_next, x, y, H_post, H_res, dx, dy, dH_post, dH_res, stream));
+}
+
+mhc_status mhc_pre_bwd(const mhc_desc* d, const void* dh, const void* x, const float* phi,
+                       const float* bias, const float* dH_post, const float* dH_res, void* dx,
+                       float* dphi, float* dbias, float* dalpha, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  mhc_status st = check_desc(d);
+  if (st != MHC_OK) return st;
+  if (d->sinkhorn_iters > kMaxBwdIters) return MHC_ERR_UNSUPPORTED;
+  if (!aligned16(dh) || !aligned16(x) || !aligned16(phi) || !aligned16(bias) ||
+      !aligned16(dH_post) || !aligned16(dH_res) || !aligned16(dx) || !aligned16(dphi) ||
+      !aligned16(dbias))
+    return MHC_ERR_INVALID_ARG;
+  if (dalpha != nullptr && (reinterpret_cast<uintptr_t>(dalpha) & 3u) != 0) return MHC_ERR_INVALID_ARG;
+  const size_t b = io_bytes(d), T = (size_t)d->T, N = (size_t)d->N, D = (size_t)d->D;
+  if (overlaps(dx, T * N * D * b, x, T * N * D * b) || overlaps(dx, T * N * D * b, dh, T * D * b))
+    return MHC_ERR_INVALID_ARG;
+  if (!workspace_ok(workspace, workspace_bytes, mhc::pre_bwd_workspace_bytes(*d)))
+    return MHC_ERR_INVALID_ARG;
+  return from_hip(mhc::launch_pre_bwd(*d, dh, x, phi, bias, dH_post, dH_res, dx, dphi, dbias,
+                                      dalpha, workspace, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,130 @@
+// Device-side helpers shared by the mHC kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace mhc {
+
+constexpr int kWave = 64;
+
+enum Io : int { kF32 = 0, kBF16 = 1 };
+
+template <int IO>
+struct IoT;
+template <>
+struct IoT<kF32> {
+  using elem = float;
+  static constexpr int bytes = 4;
+};
+template <>
+struct IoT<kBF16> {
+  using elem = uint16_t;
+  static constexpr int bytes = 2;
+};
+
+// bf16 → fp32 is exact: the 16 bits are the top half of the fp32 word.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 → bf16, round to nearest, ties to even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x0040u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Eight consecutive elements starting at element index `i` (i % 8 == 0,
+// 16-byte aligned base), widened to fp32.
+template <int IO>
+__device__ __forceinline__ void load8(const void* base, int64_t i, float v[8]) {
+  if constexpr (IO == kF32) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + i);
+    float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + i);
+    v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
+    v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+    v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
+    v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+  }
+}
+
+template <int IO>
+__device__ __forceinline__ void store8(void* base, int64_t i, const float v[8]) {
+  if constexpr (IO == kF32) {
+    float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + i);
+    p[0] = make_float4(v[0], v[1], v[2], v[3]);
+    p[1] = make_float4(v[4], v[5], v[6], v[7]);
+  } else {
+    uint4 w;
+    w.x = pack_bf16x2(v[0], v[1]);
+    w.y = pack_bf16x2(v[2], v[3]);
+    w.z = pack_bf16x2(v[4], v[5]);
+    w.w = pack_bf16x2(v[6], v[7]);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + i) = w;
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Sum `n` per-thread values over the block; the totals land in red[0..n) for
+// every thread.  `red` needs n * (blockDim.x / 64) floats of LDS.  Fixed
+// order: butterfly within each wave, then waves in index order.
+template <int n>
+__device__ __forceinline__ void block_sum(float (&v)[n], float* red) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int nw = blockDim.x / kWave;
+#pragma unroll
+  for (int i = 0; i < n; ++i) {
+    float s = wave_sum(v[i]);
+    if (lane == 0) red[wave * n + i] = s;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    float s = 0.f;
+    for (int w = 0; w < nw; ++w) s += red[w * n + i];
+    red[(nw - 1) * n + i] = s;  // last wave's slot holds the total (read after the barrier)
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < n; ++i) v[i] = red[(nw - 1) * n + i];
+  __syncthreads();
+}
+
+__device__ __forceinline__ float sigmoid(float z) { return 1.0f / (1.0f + expf(-z)); }
+
+// Calls f(std::integral_constant<int, N>) for the supported stream counts.
+template <typename F>
+__host__ bool dispatch_n(int n, F&& f) {
+  switch (n) {
+    case 1: f(std::integral_constant<int, 1>{}); return true;
+    case 2: f(std::integral_constant<int, 2>{}); return true;
+    case 4: f(std::integral_constant<int, 4>{}); return true;
+    case 8: f(std::integral_constant<int, 8>{}); return true;
+    default: return false;
+  }
+}
+template <typename F>
+__host__ bool dispatch_io(int io, F&& f) {
+  switch (io) {
+    case kF32: f(std::integral_constant<int, kF32>{}); return true;
+    case kBF16: f(std::integral_constant<int, kBF16>{}); return true;
+    default: return false;
+  }
+}
+
+}  // namespace mhc

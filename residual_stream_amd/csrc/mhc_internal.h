@@ -1,0 +1,29 @@
+// Host-side launchers behind the C ABI (one per kernel family).  Each returns
+// the HIP error of its last launch; arguments are validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+#include "../../include/mhc.h"
+
+namespace mhc {
+
+size_t pre_workspace_bytes(const mhc_desc& d);
+hipError_t launch_pre(const mhc_desc& d, const void* x, const float* phi, const float* bias,
+                      void* h, float* H_pre, float* H_post, float* H_res, void* ws,
+                      hipStream_t s);
+
+hipError_t launch_post(const mhc_desc& d, const void* x, const void* y, const float* H_post,
+                       const float* H_res, void* x_next, hipStream_t s);
+
+hipError_t launch_post_bwd(const mhc_desc& d, const void* dxn, const void* x, const void* y,
+                           const float* H_post, const float* H_res, void* dx, void* dy,
+                           float* dH_post, float* dH_res, hipStream_t s);
+
+size_t pre_bwd_workspace_bytes(const mhc_desc& d);
+hipError_t launch_pre_bwd(const mhc_desc& d, const void* dh, const void* x, const float* phi,
+                          const float* bias, const float* dH_post, const float* dH_res, void* dx,
+                          float* dphi, float* dbias, float* dalpha, void* ws, hipStream_t s);
+
+}  // namespace mhc

@@ -4,7 +4,8 @@ This module holds no arithmetic of the method: it only draws random arrays and
 rounds them to the storage dtype.  Both the fp64 oracle and the HIP path consume
 exactly the arrays returned here.
 
-Recipe (one ``numpy.random.default_rng(seed)``, float64 draws in this order):
+Recipe (one ``numpy.random.default_rng(seed)``, draws in this order; the
+activations are drawn directly in float32, phi and bias in float64):
 
 * x[T,N,D] ~ N(0,1)        — the N-stream residual state
 * y[T,D] ~ N(0,1)          — the sublayer output
@@ -33,15 +34,21 @@ def round_to_bf16(a: np.ndarray) -> np.ndarray:
 
     NaN stays NaN; overflow goes to ±inf as IEEE rounding prescribes.
     """
-    f = np.ascontiguousarray(a, dtype=np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16) << 16
-    out = r.astype(np.uint32).view(np.float32).copy()
-    nan = np.isnan(f)
-    if nan.any():
-        out[nan] = np.float32("nan")
-    return out
+    f = np.array(a, dtype=np.float32, copy=True, order="C")
+    flat = f.reshape(-1)
+    u_all = flat.view(np.uint32)
+    step = 1 << 20
+    for i in range(0, flat.size, step):
+        u = u_all[i:i + step]
+        nan = np.isnan(flat[i:i + step])
+        # For every non-NaN word u + 0x7FFF + 1 stays below 2^32: uint32 arithmetic is exact.
+        lsb = (u >> 16) & np.uint32(1)
+        u += np.uint32(0x7FFF)
+        u += lsb
+        u &= np.uint32(0xFFFF0000)
+        if nan.any():
+            flat[i:i + step][nan] = np.float32("nan")
+    return f
 
 
 def to_io(a: np.ndarray, io: str) -> np.ndarray:
@@ -86,14 +93,14 @@ def make_inputs(T: int, N: int, D: int, io: str = IO_F32, seed: int = 0,
     rng = np.random.default_rng(seed)
     K = N * D
     C = N * N + 2 * N
-    x = to_io(rng.standard_normal((T, N, D)), io)
-    y = to_io(rng.standard_normal((T, D)), io)
+    x = to_io(rng.standard_normal((T, N, D), dtype=np.float32), io)
+    y = to_io(rng.standard_normal((T, D), dtype=np.float32), io)
     phi = (rng.standard_normal((K, C)) * (1.0 / np.sqrt(K))).astype(np.float32)
     bias = (rng.standard_normal(C) * np.sqrt(0.1)).astype(np.float32)
     dh = dxn = None
     if grads:
-        dh = to_io(rng.standard_normal((T, D)), io)
-        dxn = to_io(rng.standard_normal((T, N, D)), io)
+        dh = to_io(rng.standard_normal((T, D), dtype=np.float32), io)
+        dxn = to_io(rng.standard_normal((T, N, D), dtype=np.float32), io)
     alphas = tuple(float(a) for a in alpha) if isinstance(alpha, (tuple, list)) else (float(alpha),) * 3
     return MhcInputs(T=T, N=N, D=D, io=io, x=x, y=y, phi=phi, bias=bias, alphas=alphas,
                      eps=float(eps), iters=int(iters), dh=dh, dx_next=dxn)

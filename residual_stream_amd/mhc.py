@@ -1,0 +1,231 @@
+"""Python binding of the mHC C ABI (include/mhc.h): argument marshalling only.
+
+Every step of hc_pre / hc_post and their backward runs in the gfx950 kernels of
+``libmhc.so``; this module turns torch tensors into device pointers, allocates
+outputs and workspaces with torch (the library itself never allocates), and
+passes torch's current HIP stream.  There is no fallback: if the library is
+missing or the tensors are not on the GPU, the call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (loads the HIP runtime the library binds to)
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmhc.so")
+
+MHC_F32 = 0
+MHC_BF16 = 1
+MHC_OK = 0
+MHC_ERR_INVALID_ARG = 1
+MHC_ERR_UNSUPPORTED = 2
+MHC_ERR_HIP = 3
+
+ABI_FUNCTIONS = (
+    "mhc_pre_workspace_bytes",
+    "mhc_pre",
+    "mhc_post",
+    "mhc_post_bwd",
+    "mhc_pre_bwd_workspace_bytes",
+    "mhc_pre_bwd",
+    "mhc_status_string",
+    "mhc_abi_version",
+)
+
+
+class MhcDesc(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int64),
+        ("N", ctypes.c_int32),
+        ("D", ctypes.c_int32),
+        ("io", ctypes.c_int32),
+        ("sinkhorn_iters", ctypes.c_int32),
+        ("eps", ctypes.c_float),
+        ("alpha_pre", ctypes.c_float),
+        ("alpha_post", ctypes.c_float),
+        ("alpha_res", ctypes.c_float),
+    ]
+
+
+class MhcError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+
+
+_lib = None
+_P = ctypes.c_void_p
+_DP = ctypes.POINTER(MhcDesc)
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load libmhc.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m residual_stream_amd.build`")
+    lib = ctypes.CDLL(p)
+    lib.mhc_abi_version.restype = ctypes.c_int
+    lib.mhc_abi_version.argtypes = []
+    lib.mhc_status_string.restype = ctypes.c_char_p
+    lib.mhc_status_string.argtypes = [ctypes.c_int]
+    for name in ("mhc_pre_workspace_bytes", "mhc_pre_bwd_workspace_bytes"):
+        f = getattr(lib, name)
+        f.restype = ctypes.c_size_t
+        f.argtypes = [_DP]
+    lib.mhc_pre.restype = ctypes.c_int
+    lib.mhc_pre.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.mhc_post.restype = ctypes.c_int
+    lib.mhc_post.argtypes = [_DP, _P, _P, _P, _P, _P, _P]
+    lib.mhc_post_bwd.restype = ctypes.c_int
+    lib.mhc_post_bwd.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.mhc_pre_bwd.restype = ctypes.c_int
+    lib.mhc_pre_bwd.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().mhc_status_string(int(status)).decode()
+
+
+def make_desc(T: int, N: int, D: int, io: int, iters: int = 20, eps: float = 1e-6,
+              alphas=(0.01, 0.01, 0.01)) -> MhcDesc:
+    a = tuple(alphas)
+    return MhcDesc(int(T), int(N), int(D), int(io), int(iters), float(eps), float(a[0]),
+                   float(a[1]), float(a[2]))
+
+
+def _io_of(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MHC_F32
+    if t.dtype == torch.bfloat16:
+        return MHC_BF16
+    raise TypeError(f"I/O tensors must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch tensor")
+    if not t.is_cuda:
+        raise RuntimeError("the mHC kernels need GPU tensors (no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != MHC_OK:
+        raise MhcError(status, where)
+
+
+def _f32(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype != torch.float32:
+        raise TypeError(f"{tuple(t.shape)} tensor must be float32")
+    return t
+
+
+def desc_for(x: torch.Tensor, iters: int = 20, eps: float = 1e-6, alphas=(0.01, 0.01, 0.01)):
+    T, N, D = x.shape
+    return make_desc(T, N, D, _io_of(x), iters, eps, alphas)
+
+
+def mhc_pre(x, phi, bias, *, iters=20, eps=1e-6, alphas=(0.01, 0.01, 0.01), out=None,
+            workspace=None, stream=None):
+    """hc_pre forward.  x[T,N,D] (fp32/bf16), phi[N·D,C], bias[C] fp32.
+
+    Returns (h[T,D], H_pre[T,N], H_post[T,N], H_res[T,N,N])."""
+    lib = load()
+    d = desc_for(x, iters, eps, alphas)
+    T, N, D = x.shape
+    if out is None:
+        out = (torch.empty((T, D), dtype=x.dtype, device=x.device),
+               torch.empty((T, N), dtype=torch.float32, device=x.device),
+               torch.empty((T, N), dtype=torch.float32, device=x.device),
+               torch.empty((T, N, N), dtype=torch.float32, device=x.device))
+    h, Hp, Hq, Hr = out
+    need = lib.mhc_pre_workspace_bytes(ctypes.byref(d))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    nbytes = workspace.numel() if workspace is not None else 0
+    st = lib.mhc_pre(ctypes.byref(d), _ptr(x), _ptr(_f32(phi)), _ptr(_f32(bias)), _ptr(h), _ptr(Hp),
+                     _ptr(Hq), _ptr(Hr), _ptr(workspace), nbytes, _stream(stream))
+    _check(st, "mhc_pre")
+    return out
+
+
+def mhc_post(x, y, H_post, H_res, *, out=None, stream=None):
+    """hc_post forward: returns x_next[T,N,D] in x's dtype."""
+    lib = load()
+    d = desc_for(x)
+    if out is None:
+        out = torch.empty_like(x)
+    st = lib.mhc_post(ctypes.byref(d), _ptr(x), _ptr(y), _ptr(_f32(H_post)), _ptr(_f32(H_res)),
+                      _ptr(out), _stream(stream))
+    _check(st, "mhc_post")
+    return out
+
+
+def mhc_post_bwd(dx_next, x, y, H_post, H_res, *, out=None, stream=None):
+    """hc_post backward: returns (dx[T,N,D], dy[T,D], dH_post[T,N], dH_res[T,N,N])."""
+    lib = load()
+    d = desc_for(x)
+    T, N, D = x.shape
+    if out is None:
+        out = (torch.empty_like(x), torch.empty_like(y),
+               torch.empty((T, N), dtype=torch.float32, device=x.device),
+               torch.empty((T, N, N), dtype=torch.float32, device=x.device))
+    dx, dy, dHp, dHr = out
+    st = lib.mhc_post_bwd(ctypes.byref(d), _ptr(dx_next), _ptr(x), _ptr(y), _ptr(_f32(H_post)),
+                          _ptr(_f32(H_res)), _ptr(dx), _ptr(dy), _ptr(dHp), _ptr(dHr),
+                          _stream(stream))
+    _check(st, "mhc_post_bwd")
+    return out
+
+
+def mhc_pre_bwd(dh, x, phi, bias, dH_post, dH_res, dx, *, iters=20, eps=1e-6,
+                alphas=(0.01, 0.01, 0.01), want_dalpha=True, out=None, workspace=None,
+                stream=None):
+    """hc_pre backward with recompute.  `dx` holds hc_post's contribution on
+    entry and the total on return (updated in place).
+
+    Returns (dx, dphi[K,C], dbias[C], dalpha[3] or None)."""
+    lib = load()
+    d = desc_for(x, iters, eps, alphas)
+    T, N, D = x.shape
+    C = N * N + 2 * N
+    if out is None:
+        out = (torch.empty((N * D, C), dtype=torch.float32, device=x.device),
+               torch.empty((C,), dtype=torch.float32, device=x.device),
+               torch.empty((4,), dtype=torch.float32, device=x.device) if want_dalpha else None)
+    dphi, dbias, dalpha = out
+    need = lib.mhc_pre_bwd_workspace_bytes(ctypes.byref(d))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    nbytes = workspace.numel() if workspace is not None else 0
+    st = lib.mhc_pre_bwd(ctypes.byref(d), _ptr(dh), _ptr(x), _ptr(_f32(phi)), _ptr(_f32(bias)),
+                         _ptr(_f32(dH_post)), _ptr(_f32(dH_res)), _ptr(dx), _ptr(dphi),
+                         _ptr(dbias), _ptr(dalpha), _ptr(workspace), nbytes, _stream(stream))
+    _check(st, "mhc_pre_bwd")
+    return dx, dphi, dbias, (dalpha[:3] if dalpha is not None else None)
+
+
+def workspace_bytes(kind: str, T: int, N: int, D: int, io: int, iters: int = 20) -> int:
+    """Workspace size for 'pre' or 'pre_bwd' (host-only query)."""
+    lib = load()
+    d = make_desc(T, N, D, io, iters)
+    f = lib.mhc_pre_workspace_bytes if kind == "pre" else lib.mhc_pre_bwd_workspace_bytes
+    return int(f(ctypes.byref(d)))

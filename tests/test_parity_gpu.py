@@ -1,0 +1,178 @@
+"""GPU parity: the C-ABI kernels against the fp64 oracle on seeded inputs.
+
+Tolerance (normwise per output tensor, max|gpu − oracle| / max|oracle|):
+1e-5 for fp32 I/O, 2e-2 for bf16 I/O with fp32 accumulation.  Small cases run
+the whole oracle; the full-size workloads compare sampled tokens (the forward
+is token-local) and, for dφ / dbias, the full fp64 oracle.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from residual_stream_amd import mhc
+from residual_stream_amd.inputs import make_inputs
+
+from mhc_testlib import (TOL, assert_close, dev, gpu_backward, gpu_forward, host,
+                         oracle_backward, oracle_forward)
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+FWD_KEYS = ("h", "H_pre", "H_post", "H_res", "x_next")
+BWD_KEYS = ("dx", "dy", "dH_post", "dH_res", "dphi", "dbias", "dalpha")
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def check_forward(inp, tokens=None):
+    _say(f"[fwd] T={inp.T} N={inp.N} D={inp.D} io={inp.io} alpha={inp.alphas[0]}")
+    g = gpu_forward(inp)
+    torch.cuda.synchronize()
+    r = oracle_forward(inp, tokens)
+    errs = {}
+    for k in FWD_KEYS:
+        got = host(g[k])
+        if tokens is not None:
+            got = got[tokens]
+        errs[k] = assert_close(k, got, r[k], TOL[inp.io])
+    return errs
+
+
+def check_backward(inp, tokens=None):
+    _say(f"[bwd] T={inp.T} N={inp.N} D={inp.D} io={inp.io} alpha={inp.alphas[0]}")
+    g = gpu_backward(inp)
+    torch.cuda.synchronize()
+    errs = {}
+    r = oracle_backward(inp)
+    for k in BWD_KEYS:
+        got, ref = host(g[k]), r[k]
+        if tokens is not None and k not in ("dphi", "dbias", "dalpha"):
+            got, ref = got[tokens], ref[tokens]
+        errs[k] = assert_close(k, got, ref, TOL[inp.io])
+    return errs
+
+
+# ------------------------------------------------------------ small cases ---
+
+def test_tiny_workload_forward_fp32():
+    # 64 tokens, 4 streams, D = 256, fp32, seed 0, alpha 0.01
+    check_forward(make_inputs(64, 4, 256, io="f32", seed=0))
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [1, 2, 4, 8])
+@pytest.mark.parametrize("T,D", [(1, 8), (3, 24), (37, 264), (130, 1032)])
+def test_forward_shapes(io, N, T, D):
+    check_forward(make_inputs(T, N, D, io=io, seed=T + N + D, alpha=1.0))
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [1, 2, 4, 8])
+@pytest.mark.parametrize("T,D", [(1, 8), (5, 40), (70, 520)])
+def test_backward_shapes(io, N, T, D):
+    check_backward(make_inputs(T, N, D, io=io, seed=100 + T + N + D, alpha=1.0, grads=True))
+
+
+@pytest.mark.parametrize("alpha", [0.01, 1.0])
+def test_tiny_workload_backward(alpha):
+    check_backward(make_inputs(64, 4, 256, io="f32", seed=0, alpha=alpha, grads=True))
+
+
+def test_forward_finite_difference_slice_bf16():
+    # The T = 4, D = 16 slice of the long-sequence backward, in bf16 I/O.
+    check_backward(make_inputs(4, 4, 16, io="bf16", seed=5, alpha=1.0, grads=True))
+
+
+def test_sinkhorn_rounds_parameter():
+    for iters in (1, 3, 64):
+        inp = make_inputs(16, 4, 64, io="f32", seed=iters, alpha=1.0, grads=True, iters=iters)
+        check_forward(inp)
+        check_backward(inp)
+
+
+def test_doubly_stochastic_on_gpu():
+    inp = make_inputs(256, 4, 512, io="f32", seed=0)
+    Hr = host(gpu_forward(inp)["H_res"])
+    assert np.all(Hr >= 0)
+    np.testing.assert_allclose(Hr.sum(-1), 1.0, atol=1e-6)
+    np.testing.assert_allclose(Hr.sum(-2), 1.0, atol=1e-6)
+    Hp = host(gpu_forward(inp)["H_pre"])
+    Hq = host(gpu_forward(inp)["H_post"])
+    assert np.all((Hp > 0) & (Hp < 1)) and np.all((Hq > 0) & (Hq < 2))
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_post_hand_fed_identity_and_permutation_bit_exact(io):
+    inp = make_inputs(33, 4, 264, io=io, seed=7)
+    x, y = dev(inp.x, io), dev(inp.y, io)
+    zeros = torch.zeros((33, 4), dtype=torch.float32, device="cuda")
+    eye = torch.eye(4, device="cuda").expand(33, 4, 4).contiguous()
+    xn = mhc.mhc_post(x, y, zeros, eye)
+    assert torch.equal(xn, x)
+    perm = [2, 3, 1, 0]
+    P = torch.eye(4, device="cuda")[perm].expand(33, 4, 4).contiguous()
+    xn = mhc.mhc_post(x, y, zeros, P)
+    assert torch.equal(xn, x[:, perm, :])
+
+
+def test_deterministic_and_side_stream():
+    inp = make_inputs(96, 4, 1024, io="bf16", seed=11, alpha=1.0, grads=True)
+    a = gpu_forward(inp)
+    b = gpu_backward(inp, a)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        a2 = gpu_forward(inp, stream=s)
+    s.synchronize()
+    for k in FWD_KEYS:
+        assert torch.equal(a[k], a2[k]), k
+    b2 = gpu_backward(inp, a)
+    torch.cuda.synchronize()
+    for k in BWD_KEYS:
+        assert torch.equal(b[k], b2[k]), k
+
+
+def test_workspace_too_small_rejected():
+    inp = make_inputs(8, 4, 64, io="f32", seed=1, grads=True)
+    x = dev(inp.x, "f32")
+    f = gpu_forward(inp)
+    need = mhc.workspace_bytes("pre_bwd", 8, 4, 64, mhc.MHC_F32)
+    ws = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+    dx = torch.zeros_like(x)
+    with pytest.raises(mhc.MhcError) as e:
+        mhc.mhc_pre_bwd(dev(inp.dh, "f32"), x, dev(inp.phi), dev(inp.bias), f["H_post"],
+                        f["H_res"], dx, workspace=ws)
+    assert e.value.status == mhc.MHC_ERR_INVALID_ARG
+
+
+def test_cpu_tensors_refused():
+    inp = make_inputs(4, 4, 16, io="f32", seed=1)
+    with pytest.raises(RuntimeError):
+        mhc.mhc_pre(torch.from_numpy(inp.x), torch.from_numpy(inp.phi), torch.from_numpy(inp.bias))
+
+
+# ----------------------------------------------------- full-size workloads ---
+
+def _sample_tokens(T, n=40, seed=0):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, 1, T - 2, T - 1], rng.choice(T, n, replace=False)]))
+
+
+@pytest.mark.parametrize("T,D,io", [(1024, 5120, "f32"), (2048, 2560, "f32"), (4096, 5120, "bf16")])
+def test_full_size_forward_sampled(T, D, io):
+    inp = make_inputs(T, 4, D, io=io, seed=0)
+    check_forward(inp, tokens=_sample_tokens(T))
+
+
+def test_full_size_backward_long_sequence_bf16():
+    # B=1, S=4096, N=4, D=5120, bf16 I/O: dx, dy, dH_* on sampled tokens, dφ / dbias / dα
+    # against the full fp64 oracle.
+    inp = make_inputs(4096, 4, 5120, io="bf16", seed=0, grads=True)
+    check_backward(inp, tokens=_sample_tokens(4096))
