@@ -1,6 +1,8 @@
-// hc_pre forward (openPangu 2.0 analysis, §5.3 "mHC" formula block).
+// hc_pre forward (openPangu 2.0 analysis, §5.3 "mHC" formula block), generic
+// path for the shapes the matrix-core kernel does not cover (N ≠ 4, D not a
+// multiple of 32, very wide D).
 //
-// Generic kernel: one workgroup per token.  Pass 1 reads the token's N·D
+// Kernel: one workgroup per token.  Pass 1 reads the token's N·D
 // elements once, accumulating the sum of squares and the C = N²+2N raw
 // projections x·φ (φ rows come from L2); a block reduction gives the totals;
 // one thread forms the logits, gates and Sinkhorn rounds; pass 2 collapses the
@@ -80,11 +82,9 @@ __global__ __launch_bounds__(kPreThreads) void hc_pre_generic(
   }
 }
 
-size_t pre_workspace_bytes(const mhc_desc&) { return 0; }
-
-hipError_t launch_pre(const mhc_desc& d, const void* x, const float* phi, const float* bias,
-                      void* h, float* H_pre, float* H_post, float* H_res, void*,
-                      hipStream_t s) {
+hipError_t launch_pre_generic(const mhc_desc& d, const void* x, const float* phi,
+                              const float* bias, void* h, float* H_pre, float* H_post,
+                              float* H_res, hipStream_t s) {
   bool ok = dispatch_n(d.N, [&](auto n_) {
     dispatch_io(d.io, [&](auto io_) {
       constexpr int N = decltype(n_)::value;

@@ -9,6 +9,10 @@
 
 namespace mhc {
 
+// Compute units of the current device (cached per device; a property query,
+// not mutable state).
+int device_cu_count();
+
 size_t pre_workspace_bytes(const mhc_desc& d);
 hipError_t launch_pre(const mhc_desc& d, const void* x, const float* phi, const float* bias,
                       void* h, float* H_pre, float* H_post, float* H_res, void* ws,

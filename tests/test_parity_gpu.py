@@ -75,6 +75,16 @@ def test_forward_shapes(io, N, T, D):
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [2560, 5120])
+@pytest.mark.parametrize("T", [1, 5, 37, 130])
+@pytest.mark.parametrize("alpha", [0.01, 1.0])
+def test_forward_matrix_core_shapes(io, D, T, alpha):
+    # N = 4 at the Flash and Pro widths runs the tiled matrix-core kernel;
+    # token counts that are not tile multiples exercise the zero-filled tail.
+    check_forward(make_inputs(T, 4, D, io=io, seed=T + D, alpha=alpha))
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("N", [1, 2, 4, 8])
 @pytest.mark.parametrize("T,D", [(1, 8), (5, 40), (70, 520)])
 def test_backward_shapes(io, N, T, D):
