@@ -128,7 +128,10 @@ static PreBwdLayout pre_bwd_layout(const mhc_desc& d) {
   return L;
 }
 
-size_t pre_bwd_workspace_bytes(const mhc_desc& d) { return pre_bwd_layout(d).total; }
+size_t pre_bwd_workspace_bytes(const mhc_desc& d) {
+  if (pre_bwd_mfma_eligible(d)) return pre_bwd_mfma_workspace_bytes(d);
+  return pre_bwd_layout(d).total;
+}
 
 // One workgroup per token.  Pass 1: sum of squares, raw projections and
 // dH_pre[n] = <dh, x[n]>.  One thread then recomputes the coefficients,
@@ -362,6 +365,14 @@ __global__ __launch_bounds__(kBwdThreads) void bias_alpha_reduce(const float* __
 hipError_t launch_pre_bwd(const mhc_desc& d, const void* dh, const void* x, const float* phi,
                           const float* bias, const float* dH_post, const float* dH_res, void* dx,
                           float* dphi, float* dbias, float* dalpha, void* ws, hipStream_t s) {
+  if (pre_bwd_mfma_eligible(d)) {
+    float *dlog = nullptr, *dal = nullptr;
+    hipError_t e = launch_pre_bwd_mfma(d, dh, x, phi, bias, dH_post, dH_res, dx, dphi, ws, &dlog, &dal, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bias_alpha_reduce<4>), dim3(1), dim3(kBwdThreads), 0, s, dlog, dal, dbias, dalpha,
+                       (int64_t)d.T);
+    return hipGetLastError();
+  }
   const PreBwdLayout L = pre_bwd_layout(d);
   char* w = static_cast<char*>(ws);
   float* gq = reinterpret_cast<float*>(w + L.gq);

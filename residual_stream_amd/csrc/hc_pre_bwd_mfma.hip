@@ -1,0 +1,490 @@
+// hc_pre backward on the matrix cores (bf16 I/O, N = 4, D a multiple of 256).
+//
+// Exact derivative of the openPangu 2.0 analysis §5.3 formula block, with the
+// forward recomputed from x (Ascend mHC Triton article, intra-layer recompute
+// paragraph).  Three passes:
+//
+//  1. bwd_proj_kernel — split-K reduction.  A workgroup keeps one d-slice of φ
+//     (all four streams) in LDS as bf16 and streams x and dh for a range of
+//     tokens: per (token, slice) it writes the raw projections x·φ (matrix
+//     cores), the sum of squares and <dh, x[n]> (vector ALU).
+//  2. bwd_coef_kernel — per token, four lanes (one per H_res row): sums the
+//     slices, recomputes rstd, logits, gates and the Sinkhorn rounds (keeping
+//     the row/column scalings u, v of every round in LDS), walks the rounds
+//     backwards and emits G = rstd·α⊙dℓ (the token's factor in dφ and in
+//     dx̄ = G·φᵀ), β = rstd³·(dq·p)/K, H_pre, dℓ and the dα terms.
+//  3. bwd_dx_kernel — per k-slice: dx += G·φᵀ − β·x + H_pre[n]·dh (matrix
+//     cores, φ slice in LDS) and the partial dφ = Σ_t x_tᵀ G_t over its token
+//     range (matrix cores on an LDS-transposed copy of the x tile).
+// A final kernel sums the dφ partials (fixed order); dbias / dα reuse the
+// generic reductions.
+#include "mhc_coef.h"
+#include "mhc_internal.h"
+
+namespace mhc {
+namespace bwdm {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kN = 4;
+constexpr int kC = kN * kN + 2 * kN;  // 24
+constexpr int kPartStride = 32;       // floats per (slice, token): p[24], ss, dhp[4], pad
+constexpr int kSliceD = 256;          // d per projection slice (1024 k)
+constexpr int kProjThreads = 256;     // 4 waves × 16 tokens
+constexpr int kProjTokens = 256;      // tokens per projection workgroup
+
+__device__ __forceinline__ f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------- pass 1 ---
+// LDS φ slice, transposed: phiT[c][k] (c < 32, k < 1024 of the slice; the k
+// order is stream-major, k_local = n·256 + d_local), rows padded by 8 bf16.
+constexpr int kPhiTRow = 4 * kSliceD + 8;  // 24 rows of c: 49.5 KB
+
+__global__ __launch_bounds__(kProjThreads) void bwd_proj_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ dh, const float* __restrict__ phi,
+    float* __restrict__ part, int64_t T, int D) {
+  __shared__ uint16_t phiT[kC * kPhiTRow];
+  const int slice = blockIdx.x;
+  const int nslices = gridDim.x;
+  const int64_t tbeg = (int64_t)blockIdx.y * kProjTokens;
+  const int K = kN * D;
+  const int d_base = slice * kSliceD;
+
+  // φ slice → LDS (bf16, transposed)
+  for (int i = threadIdx.x; i < 4 * kSliceD * kC; i += kProjThreads) {
+    const int c = i % kC, kl = i / kC;
+    const int n = kl / kSliceD, dl = kl % kSliceD;
+    phiT[c * kPhiTRow + kl] = (uint16_t)f32_to_bf16_bits(phi[((int64_t)n * D + d_base + dl) * kC + c]);
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = lane & 15, g = lane >> 4;
+  for (int64_t t0 = tbeg + wave * 16; t0 < tbeg + kProjTokens && t0 < T; t0 += 64) {
+    const int64_t t = t0 + row;
+    const bool tok = t < T;
+    const int64_t tc = tok ? t : T - 1;  // clamp: rows past T load a valid row, results unused
+    const uint16_t* xr = x + tc * K;
+    const uint16_t* dr = dh + tc * D;
+    f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    float ss = 0.f, dhp[kN] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+    for (int db = 0; db < kSliceD / 32; ++db) {
+      const int d0 = d_base + db * 32 + 8 * g;
+      const uint4 hv = *reinterpret_cast<const uint4*>(dr + d0);
+      uint4 xv[kN];
+#pragma unroll
+      for (int n = 0; n < kN; ++n) xv[n] = *reinterpret_cast<const uint4*>(xr + (int64_t)n * D + d0);
+      const float hf[8] = {bf16_lo(hv.x), bf16_hi(hv.x), bf16_lo(hv.y), bf16_hi(hv.y),
+                           bf16_lo(hv.z), bf16_hi(hv.z), bf16_lo(hv.w), bf16_hi(hv.w)};
+#pragma unroll
+      for (int n = 0; n < kN; ++n) {
+        const int kl = n * kSliceD + db * 32 + 8 * g;
+        const uint4 b0 = *reinterpret_cast<const uint4*>(&phiT[row * kPhiTRow + kl]);
+        // columns 24..31 of the second group are zero
+        uint4 b1 = *reinterpret_cast<const uint4*>(&phiT[(16 + (row & 7)) * kPhiTRow + kl]);
+        if (row >= kC - 16) b1 = make_uint4(0, 0, 0, 0);
+        acc0 = mfma(xv[n], b0, acc0);
+        acc1 = mfma(xv[n], b1, acc1);
+        const float xf[8] = {bf16_lo(xv[n].x), bf16_hi(xv[n].x), bf16_lo(xv[n].y), bf16_hi(xv[n].y),
+                             bf16_lo(xv[n].z), bf16_hi(xv[n].z), bf16_lo(xv[n].w), bf16_hi(xv[n].w)};
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          ss += xf[v] * xf[v];
+          dhp[n] += hf[v] * xf[v];
+        }
+      }
+    }
+    // raw projections: lane holds rows (tokens) 4g..4g+3 of column `row` (+16)
+    float* pbase = part + ((int64_t)slice * T) * kPartStride;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t tq = t0 + 4 * g + q;
+      if (tq < T) {
+        pbase[tq * kPartStride + row] = acc0[q];
+        if (row < kC - 16) pbase[tq * kPartStride + 16 + row] = acc1[q];
+      }
+    }
+    // sum of squares and <dh, x[n]>: reduce over the four k-groups of a token
+    ss += __shfl_xor(ss, 16, kWave);
+    ss += __shfl_xor(ss, 32, kWave);
+#pragma unroll
+    for (int n = 0; n < kN; ++n) {
+      dhp[n] += __shfl_xor(dhp[n], 16, kWave);
+      dhp[n] += __shfl_xor(dhp[n], 32, kWave);
+    }
+    if (g == 0 && tok) {
+      pbase[t * kPartStride + kC] = ss;
+#pragma unroll
+      for (int n = 0; n < kN; ++n) pbase[t * kPartStride + kC + 1 + n] = dhp[n];
+    }
+  }
+  (void)nslices;
+}
+
+// ------------------------------------------------------------- pass 2 ---
+// Per-token outputs, fp32: coef[t][64] = G[0..31] (c ≥ 24 zero), β at 32,
+// H_pre[33..36]; dlog[t][24]; dal[t][4].
+constexpr int kCoefStride = 64;
+constexpr int kCoefThreads = 64;  // 16 tokens × 4 rows
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, true));
+}
+constexpr int kQuadXor1 = 0xB1;
+constexpr int kQuadXor2 = 0x4E;
+__device__ __forceinline__ float quad_sum(float v) {
+  v += dpp<kQuadXor1>(v);
+  v += dpp<kQuadXor2>(v);
+  return v;
+}
+__global__ __launch_bounds__(kCoefThreads) void bwd_coef_kernel(
+    const float* __restrict__ part, int nslices, const float* __restrict__ bias,
+    const float* __restrict__ dH_post, const float* __restrict__ dH_res, float* __restrict__ coef,
+    float* __restrict__ dlog, float* __restrict__ dal, int64_t T, int D, int iters, float eps,
+    float a_pre, float a_post, float a_res) {
+  extern __shared__ float hist[];  // per lane and round: u_i, then v_i (v_j read from lane j)
+  const int lane = threadIdx.x;
+  const int i = lane & 3;                 // H_res row owned by this lane
+  const int64_t t = (int64_t)blockIdx.x * 16 + (lane >> 2);
+  const bool tok = t < T;
+  const int64_t tc = tok ? t : T - 1;
+  const int K = kN * D;
+
+  // slice sums (fixed order) of this row's columns: pre i, post i, res row i, ss, dhp i
+  float p_pre = 0.f, p_post = 0.f, p_res[kN] = {0.f, 0.f, 0.f, 0.f}, ss = 0.f, dhp = 0.f;
+  for (int s = 0; s < nslices; ++s) {
+    const float* pp = part + ((int64_t)s * T + tc) * kPartStride;
+    p_pre += pp[i];
+    p_post += pp[kN + i];
+#pragma unroll
+    for (int j = 0; j < kN; ++j) p_res[j] += pp[2 * kN + i * kN + j];
+    ss += pp[kC];
+    dhp += pp[kC + 1 + i];
+  }
+  const float rstd = 1.0f / sqrtf(ss / (float)K + eps);
+  const float q_pre = rstd * p_pre, q_post = rstd * p_post;
+  const float l_pre = a_pre * q_pre + bias[i];
+  const float l_post = a_post * q_post + bias[kN + i];
+  const float s_pre = sigmoid(l_pre), s_post = sigmoid(l_post);
+  float q_res[kN], m0[kN], mx = -__builtin_huge_valf();
+#pragma unroll
+  for (int j = 0; j < kN; ++j) {
+    q_res[j] = rstd * p_res[j];
+    m0[j] = a_res * q_res[j] + bias[2 * kN + i * kN + j];
+    mx = fmaxf(mx, m0[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < kN; ++j) m0[j] = expf(m0[j] - mx);
+
+  // forward rounds on the scalings: M = diag(u)·M0·diag(v)
+  float u = 1.f, v[kN] = {1.f, 1.f, 1.f, 1.f};
+  float* h = hist + lane;  // stride 64 floats between entries
+  for (int it = 0; it < iters; ++it) {
+    float r = 0.f;
+#pragma unroll
+    for (int j = 0; j < kN; ++j) r += m0[j] * v[j];
+    u = 1.0f / r;  // row i now sums to 1
+#pragma unroll
+    for (int j = 0; j < kN; ++j) {
+      const float cj = quad_sum(u * m0[j] * v[j]);  // column j sum
+      v[j] = v[j] / cj;
+    }
+    h[(it * 2 + 0) * 64] = u;
+    h[(it * 2 + 1) * 64] = v[i];
+  }
+  const float* hq = hist + (lane & ~3);  // v_j of this token's round: hq[(it·2+1)·64 + j]
+
+  // backward: G = dL/dM, walked from the last column step to the first row step
+  float G[kN];
+#pragma unroll
+  for (int j = 0; j < kN; ++j) G[j] = tok ? dH_res[(tc * kN + i) * kN + j] : 0.f;
+  for (int it = iters - 1; it >= 0; --it) {
+    const float u_s = h[(it * 2) * 64];
+    float v_s[kN], v_p[kN], u_p;
+#pragma unroll
+    for (int j = 0; j < kN; ++j) v_s[j] = hq[(it * 2 + 1) * 64 + j];
+    if (it > 0) {
+      u_p = h[((it - 1) * 2) * 64];
+#pragma unroll
+      for (int j = 0; j < kN; ++j) v_p[j] = hq[((it - 1) * 2 + 1) * 64 + j];
+    } else {
+      u_p = 1.f;
+#pragma unroll
+      for (int j = 0; j < kN; ++j) v_p[j] = 1.f;
+    }
+    // column step: X = M0·u_s·v_p, Y = M0·u_s·v_s, divisor c_j = v_p[j]/v_s[j]
+#pragma unroll
+    for (int j = 0; j < kN; ++j) {
+      const float y = m0[j] * u_s * v_s[j];
+      const float colacc = quad_sum(G[j] * y);
+      G[j] = (G[j] - colacc) * (v_s[j] / v_p[j]);
+    }
+    // row step: X = M0·u_p·v_p, Y = M0·u_s·v_p, divisor r = u_p/u_s
+    float rowacc = 0.f;
+#pragma unroll
+    for (int j = 0; j < kN; ++j) rowacc += G[j] * (m0[j] * u_s * v_p[j]);
+    const float rinv = u_s / u_p;
+#pragma unroll
+    for (int j = 0; j < kN; ++j) G[j] = (G[j] - rowacc) * rinv;
+  }
+  // dℓ_res = dM0 ⊙ M0 (the row-max shift contributes nothing: rows are
+  // rescaled away by the first row step)
+  float dl_res[kN];
+#pragma unroll
+  for (int j = 0; j < kN; ++j) dl_res[j] = G[j] * m0[j];
+
+  const float dl_pre = dhp * s_pre * (1.0f - s_pre);
+  const float dl_post = (tok ? dH_post[tc * kN + i] : 0.f) * 2.0f * s_post * (1.0f - s_post);
+  // dq = α·dℓ; dq·p (raw p, i.e. q/rstd) summed over the token's 24 columns
+  float dqp = a_pre * dl_pre * p_pre + a_post * dl_post * p_post;
+  float da_pre = dl_pre * q_pre, da_post = dl_post * q_post, da_res = 0.f;
+#pragma unroll
+  for (int j = 0; j < kN; ++j) {
+    dqp += a_res * dl_res[j] * p_res[j];
+    da_res += dl_res[j] * q_res[j];
+  }
+  dqp = quad_sum(dqp);
+  da_pre = quad_sum(da_pre);
+  da_post = quad_sum(da_post);
+  da_res = quad_sum(da_res);
+  if (tok) {
+    float* co = coef + t * kCoefStride;
+    co[i] = rstd * a_pre * dl_pre;
+    co[kN + i] = rstd * a_post * dl_post;
+#pragma unroll
+    for (int j = 0; j < kN; ++j) co[2 * kN + i * kN + j] = rstd * a_res * dl_res[j];
+    co[kC + i] = 0.f;
+    co[kC + 4 + i] = 0.f;
+    if (i == 0) co[32] = rstd * rstd * rstd * dqp / (float)K;
+    co[33 + i] = s_pre;
+    float* dl = dlog + t * kC;
+    dl[i] = dl_pre;
+    dl[kN + i] = dl_post;
+#pragma unroll
+    for (int j = 0; j < kN; ++j) dl[2 * kN + i * kN + j] = dl_res[j];
+    if (i == 0) {
+      dal[t * 4 + 0] = da_pre;
+      dal[t * 4 + 1] = da_post;
+      dal[t * 4 + 2] = da_res;
+      dal[t * 4 + 3] = 0.f;
+    }
+  }
+}
+
+// ------------------------------------------------------------- pass 3 ---
+constexpr int kDxThreads = 256;  // 4 waves × 16 tokens
+constexpr int kDxK = 128;        // k per slice (32 d of each stream)
+constexpr int kDxTile = 64;      // tokens per tile
+constexpr int kPhiRow = 40;      // bf16 per φ row in LDS (32 + pad)
+constexpr int kGRow = 40;        // bf16 per G row (32 c + pad)
+constexpr int kGTRow = 72;       // bf16 per Gᵀ row (64 t + pad)
+constexpr int kXTRow = 72;       // bf16 per xᵀ row (64 t + pad)
+
+__global__ __launch_bounds__(kDxThreads) void bwd_dx_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ dh, const float* __restrict__ phi,
+    const float* __restrict__ coef, uint16_t* __restrict__ dx, float* __restrict__ dphi_part,
+    int64_t T, int D, int64_t tok_per_split) {
+  __shared__ uint16_t phis[kDxK * kPhiRow];     // φ[k][c], bf16
+  __shared__ uint16_t Gs[kDxTile * kGRow];      // G[t][c], bf16
+  __shared__ uint16_t GTs[32 * kGTRow];         // Gᵀ[c][t], bf16
+  __shared__ uint16_t xTs[kDxK * kXTRow];       // xᵀ[k][t], bf16
+  __shared__ float betas[kDxTile];
+  __shared__ float hps[kDxTile * kN];
+
+  const int K = kN * D;
+  const int dpk = kDxK / kN;                      // 64 d per stream in this slice
+  const int sl = blockIdx.x;                      // k-slice: d in [sl·64, sl·64+64), all streams
+  const int d_base = sl * dpk;
+  const int64_t tb = (int64_t)blockIdx.y * tok_per_split;
+  int64_t te = tb + tok_per_split;
+  if (te > T) te = T;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = lane & 15, g = lane >> 4;
+
+  // φ slice (k_local = n·64 + d_local) → LDS as bf16, c ≥ 24 zero
+  for (int i = threadIdx.x; i < kDxK * 32; i += kDxThreads) {
+    const int c = i & 31, kl = i >> 5;
+    const int n = kl / dpk, dl = kl % dpk;
+    float v = 0.f;
+    if (c < kC) v = phi[((int64_t)n * D + d_base + dl) * kC + c];
+    phis[kl * kPhiRow + c] = (uint16_t)f32_to_bf16_bits(v);
+  }
+
+  // dφ accumulators: wave w owns k-blocks w and w+4 (16 k each) × 2 c-groups
+  constexpr int kKB = kDxK / 16 / 4;  // k-blocks per wave
+  f32x4_t dacc[kKB][2];
+#pragma unroll
+  for (int a = 0; a < kKB; ++a) dacc[a][0] = dacc[a][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int64_t t0 = tb; t0 < te; t0 += kDxTile) {
+    __syncthreads();  // previous tile's readers of Gs / GTs / xTs are done
+    // stage G (bf16, both orientations), β and H_pre of the tile's tokens
+    for (int i = threadIdx.x; i < kDxTile * 32; i += kDxThreads) {
+      const int tt = i >> 5, c = i & 31;
+      const int64_t t = t0 + tt;
+      const float gv = t < te ? coef[t * kCoefStride + c] : 0.f;
+      const uint16_t gb = (uint16_t)f32_to_bf16_bits(gv);
+      Gs[tt * kGRow + c] = gb;
+      GTs[c * kGTRow + tt] = gb;
+    }
+    if (threadIdx.x < kDxTile) {
+      const int64_t t = t0 + threadIdx.x;
+      betas[threadIdx.x] = t < te ? coef[t * kCoefStride + 32] : 0.f;
+#pragma unroll
+      for (int n = 0; n < kN; ++n) hps[threadIdx.x * kN + n] = t < te ? coef[t * kCoefStride + 33 + n] : 0.f;
+    }
+    __syncthreads();
+
+    // dx for this wave's 16 tokens, k-block by k-block
+    const int tl = wave * 16 + row;  // token (local) of this lane's D column
+    const int64_t t = t0 + tl;
+    const bool tok = t < te;
+    const uint4 gb = *reinterpret_cast<const uint4*>(&Gs[tl * kGRow + 8 * g]);  // B: Gᵀ[c][t]
+    const float beta = betas[tl];
+#pragma unroll
+    for (int kb = 0; kb < kDxK / 16; ++kb) {
+      // A: φ rows k = kb·16 + row, c = 8g..8g+7
+      const uint4 af = *reinterpret_cast<const uint4*>(&phis[(kb * 16 + row) * kPhiRow + 8 * g]);
+      const f32x4_t dxb = mfma(af, gb, f32x4_t{0.f, 0.f, 0.f, 0.f});
+      // this lane: k_local = kb·16 + 4g + q (q = 0..3), token tl
+      const int kl = kb * 16 + 4 * g;
+      const int n = kl / dpk, dl = kl % dpk;
+      const int64_t xo = (tok ? t : t0) * K + (int64_t)n * D + d_base + dl;
+      const int64_t ho = (tok ? t : t0) * D + d_base + dl;
+      const uint2 xv = *reinterpret_cast<const uint2*>(x + xo);
+      const uint2 hv = *reinterpret_cast<const uint2*>(dh + ho);
+      const uint2 dv = *reinterpret_cast<const uint2*>(dx + xo);
+      const float xf[4] = {bf16_lo(xv.x), bf16_hi(xv.x), bf16_lo(xv.y), bf16_hi(xv.y)};
+      const float hf[4] = {bf16_lo(hv.x), bf16_hi(hv.x), bf16_lo(hv.y), bf16_hi(hv.y)};
+      const float df[4] = {bf16_lo(dv.x), bf16_hi(dv.x), bf16_lo(dv.y), bf16_hi(dv.y)};
+      const float hp = hps[tl * kN + n];
+      float o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = df[q] + dxb[q] - beta * xf[q] + hp * hf[q];
+      if (tok)
+        *reinterpret_cast<uint2*>(dx + xo) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+      // xᵀ tile for dφ (zeros for tokens past the range)
+      const uint16_t xb[4] = {(uint16_t)(xv.x & 0xffffu), (uint16_t)(xv.x >> 16),
+                              (uint16_t)(xv.y & 0xffffu), (uint16_t)(xv.y >> 16)};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xTs[(kl + q) * kXTRow + tl] = tok ? xb[q] : (uint16_t)0;
+    }
+    __syncthreads();
+
+    // dφ[k][c] += Σ_t x[t][k]·G[t][c] over the tile: K-dim = 32 tokens per MFMA
+#pragma unroll
+    for (int a = 0; a < kKB; ++a) {
+      const int kb = wave + 4 * a;
+#pragma unroll
+      for (int ts = 0; ts < kDxTile / 32; ++ts) {
+        const uint4 af = *reinterpret_cast<const uint4*>(&xTs[(kb * 16 + row) * kXTRow + ts * 32 + 8 * g]);
+#pragma unroll
+        for (int cg = 0; cg < 2; ++cg) {
+          const uint4 bf = *reinterpret_cast<const uint4*>(&GTs[(cg * 16 + row) * kGTRow + ts * 32 + 8 * g]);
+          // A = xᵀ[k][t], B = G[t][c] read as Gᵀ[c][t]: lane holds column c = row, t = 8g..
+          dacc[a][cg] = mfma(af, bf, dacc[a][cg]);
+        }
+      }
+    }
+  }
+  // partial dφ of this (slice, token split): lane holds rows k = 4g+q, column c = row (+16)
+#pragma unroll
+  for (int a = 0; a < kKB; ++a) {
+    const int kb = wave + 4 * a;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int kl = kb * 16 + 4 * g + q;
+      const int n = kl / dpk, dl = kl % dpk;
+      const int64_t k = (int64_t)n * D + d_base + dl;
+      float* dst = dphi_part + ((int64_t)blockIdx.y * K + k) * kC;
+      dst[row] = dacc[a][0][q];
+      if (row < kC - 16) dst[16 + row] = dacc[a][1][q];
+    }
+  }
+}
+
+// dφ = Σ_s part[s] in split order
+__global__ __launch_bounds__(256) void dphi_sum_kernel(const float* __restrict__ part,
+                                                       float* __restrict__ dphi, int64_t KC, int S) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= KC) return;
+  float s = 0.f;
+  for (int j = 0; j < S; ++j) s += part[(int64_t)j * KC + i];
+  dphi[i] = s;
+}
+
+static size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+struct Layout {
+  int S, TS;
+  size_t part, coef, dlog, dal, dphi, total;
+};
+
+static Layout layout(const mhc_desc& d) {
+  Layout L;
+  const size_t T = (size_t)d.T, K = (size_t)kN * d.D;
+  L.S = d.D / kSliceD;
+  int64_t ts = (d.T + 1023) / 1024;
+  L.TS = (int)(ts < 1 ? 1 : (ts > 8 ? 8 : ts));
+  L.part = 0;
+  L.coef = L.part + align256((size_t)L.S * T * kPartStride * 4);
+  L.dlog = L.coef + align256(T * kCoefStride * 4);
+  L.dal = L.dlog + align256(T * kC * 4);
+  L.dphi = L.dal + align256(T * 4 * 4);
+  L.total = L.dphi + align256((size_t)L.TS * K * kC * 4);
+  return L;
+}
+
+}  // namespace bwdm
+
+bool pre_bwd_mfma_eligible(const mhc_desc& d) {
+  return d.N == 4 && d.io == kBF16 && d.D % bwdm::kSliceD == 0 && d.sinkhorn_iters <= 64;
+}
+
+size_t pre_bwd_mfma_workspace_bytes(const mhc_desc& d) { return bwdm::layout(d).total; }
+
+hipError_t launch_pre_bwd_mfma(const mhc_desc& d, const void* dh, const void* x, const float* phi,
+                               const float* bias, const float* dH_post, const float* dH_res,
+                               void* dx, float* dphi, void* ws, float** dlog_out, float** dal_out,
+                               hipStream_t s) {
+  using namespace bwdm;
+  const Layout L = layout(d);
+  char* w = static_cast<char*>(ws);
+  float* part = reinterpret_cast<float*>(w + L.part);
+  float* coef = reinterpret_cast<float*>(w + L.coef);
+  float* dlog = reinterpret_cast<float*>(w + L.dlog);
+  float* dal = reinterpret_cast<float*>(w + L.dal);
+  float* dphi_part = reinterpret_cast<float*>(w + L.dphi);
+  *dlog_out = dlog;
+  *dal_out = dal;
+  const int64_t T = d.T;
+  const int K = kN * d.D;
+  hipLaunchKernelGGL(bwd_proj_kernel, dim3((unsigned)L.S, (unsigned)((T + kProjTokens - 1) / kProjTokens)),
+                     dim3(kProjThreads), 0, s, static_cast<const uint16_t*>(x),
+                     static_cast<const uint16_t*>(dh), phi, part, T, d.D);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t hist_bytes = (size_t)d.sinkhorn_iters * 2 * 64 * sizeof(float);
+  hipLaunchKernelGGL(bwd_coef_kernel, dim3((unsigned)((T + 15) / 16)), dim3(kCoefThreads), hist_bytes,
+                     s, part, L.S, bias, dH_post, dH_res, coef, dlog, dal, T, d.D, d.sinkhorn_iters,
+                     d.eps, d.alpha_pre, d.alpha_post, d.alpha_res);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t tps = ((T + L.TS - 1) / L.TS + kDxTile - 1) / kDxTile * kDxTile;
+  hipLaunchKernelGGL(bwd_dx_kernel, dim3((unsigned)(K / kDxK), (unsigned)L.TS), dim3(kDxThreads), 0, s,
+                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dh), phi, coef,
+                     static_cast<uint16_t*>(dx), dphi_part, T, d.D, tps);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t KC = (int64_t)K * kC;
+  hipLaunchKernelGGL(dphi_sum_kernel, dim3((unsigned)((KC + 255) / 256)), dim3(256), 0, s, dphi_part,
+                     dphi, KC, L.TS);
+  return hipGetLastError();
+}
+
+}  // namespace mhc

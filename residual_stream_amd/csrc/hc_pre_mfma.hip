@@ -32,6 +32,9 @@ constexpr int kMfmaWaves = 8;
 constexpr int kMfmaThreads = kMfmaWaves * kWave;
 constexpr int kN4 = 4;
 constexpr int kC4 = kN4 * kN4 + 2 * kN4;  // 24 logit columns
+#ifndef PRE_RING_VGPRS
+#define PRE_RING_VGPRS 36  // VGPRs per lane for in-flight φ fragments
+#endif
 
 template <int TM>
 struct PreTile {
@@ -81,36 +84,43 @@ __global__ __launch_bounds__(256) void phi_pack_kernel(const float* __restrict__
 
 // ------------------------------------------------------------ main kernel ---
 
-// LDS: per buffer, raw projection partials red[wave][range][token][32] and
-// sums of squares ss[wave][token]; two buffers so that wave 0 can finish the
-// previous tile's Sinkhorn while the others reduce the next tile.
+// LDS per buffer: raw projection partials red[wave][range][token][32], sums
+// of squares ss[wave][token], then per-token totals tot[token][32] (column 24
+// holds the sum of squares).  Two buffers, so wave 0 can finish the previous
+// tile's Sinkhorn while the other waves already reduce the next tile.
 template <int TM>
 struct PreLds {
   static constexpr int R = 16 / TM;
   static constexpr int kRed = kMfmaWaves * R * TM * 32;
   static constexpr int kSs = kMfmaWaves * TM;
-  static constexpr int kBuf = kRed + kSs;
+  static constexpr int kTot = TM * 32;
+  static constexpr int kBuf = kRed + kSs + kTot;
 };
 
-template <int TM>
-__device__ __forceinline__ float lds_ss(const float* buf, int tt) {
-  const float* ss = buf + PreLds<TM>::kRed;
-  float s = 0.f;
-#pragma unroll
-  for (int w = 0; w < kMfmaWaves; ++w) s += ss[w * TM + tt];
-  return s;
+// Lane exchanges through DPP (a VALU operand modifier, no LDS round trip):
+// quad_perm(1,0,3,2) swaps neighbours, quad_perm(2,3,0,1) swaps pairs,
+// row_ror:n rotates each 16-lane row by n.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, true));
 }
+constexpr int kDppQuadXor1 = 0xB1;
+constexpr int kDppQuadXor2 = 0x4E;
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;
 
-// Full raw projection p_c of token tt: sum over waves and ranges, fixed order.
+// Sum over the lanes l, l±TM, l±2TM, ... of one 16-lane row; rotating by TM
+// and its multiples visits exactly that orbit.  Result in every lane.
 template <int TM>
-__device__ __forceinline__ float lds_p(const float* buf, int tt, int c) {
-  constexpr int R = 16 / TM;
-  float s = 0.f;
-#pragma unroll
-  for (int w = 0; w < kMfmaWaves; ++w)
-#pragma unroll
-    for (int r = 0; r < R; ++r) s += buf[((w * R + r) * TM + tt) * 32 + c];
-  return s;
+__device__ __forceinline__ float row_orbit_sum(float v) {
+  if constexpr (TM == 4) {
+    v += dpp<kDppRowRor4>(v);
+    v += dpp<kDppRowRor8>(v);
+  } else if constexpr (TM == 8) {
+    v += dpp<kDppRowRor8>(v);
+  }
+  return v;
 }
 
 // A zero the compiler cannot see through, produced once per tile, so that
@@ -127,13 +137,23 @@ __device__ __forceinline__ int opaque_zero() {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+// voff: per-lane offset (VGPR); soff: wave-uniform offset (SGPR), kept out
+// of VGPRs so that unrolled loads share one address register.
+__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
   typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// NB = d-blocks (32 d each) per wave, the same for all 8 waves: D = 256·NB.
+// 1/(1+e^-z) with the hardware reciprocal (1 ulp) instead of the IEEE division sequence.
+__device__ __forceinline__ float fast_sigmoid(float z) { return __builtin_amdgcn_rcpf(1.0f + expf(-z)); }
+
+__device__ __forceinline__ f32x4_t mfma_bf16(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// NB = 32-wide d-blocks per wave, the same for all 8 waves: D = 256·NB.
 template <int IO, int TM, int NB>
 __global__ __launch_bounds__(kMfmaThreads, 1) void hc_pre_mfma_kernel(
     const void* __restrict__ x, const uint4* __restrict__ phip, const float* __restrict__ bias,
@@ -147,24 +167,25 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void hc_pre_mfma_kernel(
   constexpr int E = IO == kF32 ? 4 : 2;   // bytes per element
   constexpr int D = 256 * NB;
   constexpr int K = kN4 * D;
+  constexpr int NS = NB * SPB;                        // k-steps per wave
   constexpr uint32_t kStepBytes = CG * PS * 64 * 16;  // packed φ per k-step
-  __shared__ float lds[2 * PreLds<TM>::kBuf];
+  constexpr int LA = (PRE_RING_VGPRS / (CG * PS * 4)) > 1 ? (PRE_RING_VGPRS / (CG * PS * 4)) : 1;  // φ look-ahead
+  constexpr int L = PreLds<TM>::kBuf;
+  __shared__ float lds[2 * L];
+  __shared__ float bias_s[32];
 
-  const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int row = lane & 15;      // MFMA A row
-  const int g = lane >> 4;        // k group (8 consecutive d)
-  const int tt = row % TM;        // token within the tile
-  const int rr = row / TM;        // stream range of this lane's A rows
-  const int b0 = wave * NB;       // first d-block of this wave
+  const int b0 = wave * NB;   // first d-block of this wave
   const int64_t ntiles = (T + TM - 1) / TM;
   const float rK = 1.0f / (float)K;
 
   // φ of this wave's d-blocks: one resource, lane offset + per-step constants.
-  const uint4* phw = phip + (int64_t)b0 * SPB * (CG * PS * 64);
-  const __amdgpu_buffer_rsrc_t rphi = make_rsrc(phw, NB * SPB * kStepBytes);
-  // x offset of this lane inside a tile (bytes): token tt, stream range rr, group g.
-  const uint32_t xlane = (uint32_t)(((tt * kN4 + rr) * D + 32 * b0 + 8 * g) * E);
+  const __amdgpu_buffer_rsrc_t rphi =
+      make_rsrc(phip + (int64_t)b0 * SPB * (CG * PS * 64), NS * kStepBytes);
+
+  // bias in LDS: reading it there never waits behind the x loads in flight
+  if (threadIdx.x < 32) bias_s[threadIdx.x] = threadIdx.x < kC4 ? bias[threadIdx.x] : 0.f;
+  __syncthreads();
 
   uint4 xr[NB][SPB][XW];
   int buf = 0;
@@ -173,63 +194,71 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void hc_pre_mfma_kernel(
   for (int64_t tile = blockIdx.x; tile < ntiles || prev_tile >= 0; tile += gridDim.x) {
     const bool have = tile < ntiles;
     const int z = opaque_zero();
+    // Lane-derived values are rebuilt from the lane id each tile (a few VALU ops)
+    // rather than kept live across the loop beside the 160 VGPRs of x.
+    const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, (unsigned)z));
+    const int tid = wave * 64 + lane;
+    const int row = lane & 15;  // MFMA A row
+    const int g = lane >> 4;    // k group (8 consecutive d)
+    const int tt = row % TM;    // token within the tile
+    const int rr = row / TM;    // stream range of this lane's A rows
+    // x offset of this lane inside a tile (bytes): token tt, stream range rr, group g
+    const uint32_t xlane = (uint32_t)(((tt * kN4 + rr) * D + 32 * b0 + 8 * g) * E);
     const int64_t t0 = tile * TM;
     const int64_t my_t = t0 + tt;
     const bool tok_ok = have && my_t < T;
 
-    // ---- 1. issue every x load of this tile (kept in VGPRs until the collapse);
-    // rows past the last token fall outside the resource and read as zero.
+    // ---- 1. issue every x load of this tile (kept in VGPRs until the
+    // collapse); rows past the last token fall outside the resource and read
+    // as zero.
     if (have) {
       const int64_t valid = (T - t0) < TM ? (T - t0) : TM;
       const __amdgpu_buffer_rsrc_t rx =
           make_rsrc(static_cast<const char*>(x) + t0 * (int64_t)K * E, (uint32_t)(valid * K * E));
-      const uint32_t xo = xlane + z;
+      const uint32_t xo = xlane;
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int sp = 0; sp < SPB; ++sp) {
-          const uint32_t off = xo + (uint32_t)((sp * R * D + 32 * b) * E);
+        for (int sp = 0; sp < SPB; ++sp)
 #pragma unroll
-          for (int q = 0; q < XW; ++q) xr[b][sp][q] = ld16(rx, off + 16 * q);
-        }
-      }
+          for (int q = 0; q < XW; ++q)
+            xr[b][sp][q] = ld16(rx, xo + (uint32_t)(32 * b * E + 16 * q), (uint32_t)(sp * R * D * E) + z);
     }
 
-    // ---- 2. wave 0 finishes the previous tile: H_post, Sinkhorn, coefficient stores
+    // ---- 2. wave 0 finishes the previous tile: H_post, Sinkhorn, stores of the
+    // coefficients.  LDS reads and DPP only, so nothing waits for the loads.
     if (prev_tile >= 0 && wave == 0) {
-      const float* pb = lds + (buf ^ 1) * PreLds<TM>::kBuf;
-      const int tk = lane / kN4, i = lane % kN4;  // token, H_res row
+      const float* tot = lds + (buf ^ 1) * L + PreLds<TM>::kRed + PreLds<TM>::kSs;
+      const int tk = (lane / kN4) % TM, i = lane % kN4;  // token, H_res row
       const int64_t t = prev_tile * TM + tk;
-      if (lane < TM * kN4) {
-        const float rstd = 1.0f / sqrtf(lds_ss<TM>(pb, tk) * rK + eps);
-        const float lp = a_pre * (rstd * lds_p<TM>(pb, tk, i)) + bias[i];
-        const float lq = a_post * (rstd * lds_p<TM>(pb, tk, kN4 + i)) + bias[kN4 + i];
-        float m[kN4], mx = -__builtin_huge_valf();
+      const float rstd = __builtin_amdgcn_rsqf(tot[tk * 32 + kC4] * rK + eps);
+      const float lp = a_pre * (rstd * tot[tk * 32 + i]) + bias_s[i];
+      const float lq = a_post * (rstd * tot[tk * 32 + kN4 + i]) + bias_s[kN4 + i];
+      float m[kN4], mx = -__builtin_huge_valf();
+#pragma unroll
+      for (int j = 0; j < kN4; ++j) {
+        const int c = 2 * kN4 + i * kN4 + j;
+        m[j] = a_res * (rstd * tot[tk * 32 + c]) + bias_s[c];
+        mx = fmaxf(mx, m[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < kN4; ++j) m[j] = expf(m[j] - mx);
+      for (int it = 0; it < iters; ++it) {
+        const float rinv = __builtin_amdgcn_rcpf((m[0] + m[1]) + (m[2] + m[3]));
+#pragma unroll
+        for (int j = 0; j < kN4; ++j) m[j] *= rinv;
 #pragma unroll
         for (int j = 0; j < kN4; ++j) {
-          const int c = 2 * kN4 + i * kN4 + j;
-          m[j] = a_res * (rstd * lds_p<TM>(pb, tk, c)) + bias[c];
-          mx = fmaxf(mx, m[j]);
+          // column sum over the 4 lanes (rows) of this token
+          const float s1 = m[j] + dpp<kDppQuadXor1>(m[j]);
+          const float s = s1 + dpp<kDppQuadXor2>(s1);
+          m[j] *= __builtin_amdgcn_rcpf(s);
         }
-#pragma unroll
-        for (int j = 0; j < kN4; ++j) m[j] = expf(m[j] - mx);
-        for (int it = 0; it < iters; ++it) {
-          const float rinv = 1.0f / ((m[0] + m[1]) + (m[2] + m[3]));
-#pragma unroll
-          for (int j = 0; j < kN4; ++j) m[j] *= rinv;
-#pragma unroll
-          for (int j = 0; j < kN4; ++j) {
-            // column sum over the 4 lanes (rows) of this token, fixed pairing order
-            const float s1 = m[j] + __shfl_xor(m[j], 1, kWave);
-            const float s = s1 + __shfl_xor(s1, 2, kWave);
-            m[j] *= 1.0f / s;
-          }
-        }
-        if (t < T) {
-          H_pre[t * kN4 + i] = sigmoid(lp);
-          H_post[t * kN4 + i] = 2.0f * sigmoid(lq);
-          reinterpret_cast<float4*>(H_res)[t * kN4 + i] = make_float4(m[0], m[1], m[2], m[3]);
-        }
+      }
+      if (lane < TM * kN4 && t < T) {
+        H_pre[t * kN4 + i] = fast_sigmoid(lp);
+        H_post[t * kN4 + i] = 2.0f * fast_sigmoid(lq);
+        reinterpret_cast<float4*>(H_res)[t * kN4 + i] = make_float4(m[0], m[1], m[2], m[3]);
       }
     }
     if (!have) break;
@@ -242,14 +271,12 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void hc_pre_mfma_kernel(
     for (int cg = 0; cg < CG; ++cg) acc[cg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float ss = 0.f;
     {
-      constexpr int NS = NB * SPB;
-      constexpr int LA = (48 / (CG * PS * 4)) > 1 ? (48 / (CG * PS * 4)) : 1;  // look-ahead k-steps (~48 VGPRs)
-      const uint32_t po = (uint32_t)(lane * 16 + z);
+      const uint32_t po = (uint32_t)(lane * 16);
       uint4 ring[LA][CG * PS];
 #pragma unroll
       for (int s0 = 0; s0 < LA; ++s0)
 #pragma unroll
-        for (int f = 0; f < CG * PS; ++f) ring[s0][f] = ld16(rphi, po + s0 * kStepBytes + f * 1024);
+        for (int f = 0; f < CG * PS; ++f) ring[s0][f] = ld16(rphi, po + f * 1024, s0 * kStepBytes + z);
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
         const int b = st / SPB, sp = st % SPB, slot = st % LA;
@@ -259,7 +286,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void hc_pre_mfma_kernel(
         if (st + LA < NS) {
 #pragma unroll
           for (int f = 0; f < CG * PS; ++f)
-            ring[slot][f] = ld16(rphi, po + (st + LA) * kStepBytes + f * 1024);
+            ring[slot][f] = ld16(rphi, po + f * 1024, (st + LA) * kStepBytes + z);
         }
         // keep the look-ahead loads here: without this fence the scheduler sinks
         // them next to their use and only one L2 round trip is in flight
@@ -283,13 +310,9 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void hc_pre_mfma_kernel(
           const uint4 alo = make_uint4(lo[0], lo[1], lo[2], lo[3]);
 #pragma unroll
           for (int cg = 0; cg < CG; ++cg) {
-            const uint4 bh = cur[cg * PS + 0], bl = cur[cg * PS + 1];
-            acc[cg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8_t, ahi), __builtin_bit_cast(bf16x8_t, bh), acc[cg], 0, 0, 0);
-            acc[cg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8_t, ahi), __builtin_bit_cast(bf16x8_t, bl), acc[cg], 0, 0, 0);
-            acc[cg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8_t, alo), __builtin_bit_cast(bf16x8_t, bh), acc[cg], 0, 0, 0);
+            acc[cg] = mfma_bf16(ahi, cur[cg * PS + 0], acc[cg]);
+            acc[cg] = mfma_bf16(ahi, cur[cg * PS + 1], acc[cg]);
+            acc[cg] = mfma_bf16(alo, cur[cg * PS + 0], acc[cg]);
           }
         } else {
           const uint4 a = xr[b][sp][0];
@@ -300,38 +323,54 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void hc_pre_mfma_kernel(
             ss += lo * lo + hi * hi;
           }
 #pragma unroll
-          for (int cg = 0; cg < CG; ++cg)
-            acc[cg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, cur[cg]), acc[cg], 0, 0, 0);
+          for (int cg = 0; cg < CG; ++cg) acc[cg] = mfma_bf16(a, cur[cg], acc[cg]);
         }
       }
     }
 
-    // ---- 4. partials to LDS (diagonal range blocks only), then one barrier
-    float* rb = lds + buf * PreLds<TM>::kBuf;
+    // ---- 4. partials to LDS (diagonal range blocks only); sum of squares over
+    // the lanes of one token (row orbit, then the four 16-lane rows)
+    float* rb = lds + buf * L;
 #pragma unroll
     for (int cg = 0; cg < CG; ++cg) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int i = 4 * g + q;      // D row held by this lane
-        const int j = row;            // D column held by this lane
+        const int i = 4 * g + q;  // D row held by this lane
+        const int j = row;        // D column held by this lane
         const int c = cg * TM + (j % TM);
         if ((i / TM) == (j / TM) && c < kC4)
           rb[((wave * R + i / TM) * TM + (i % TM)) * 32 + c] = acc[cg][q];
       }
     }
-#pragma unroll
-    for (int m = TM; m < 64; m <<= 1) ss += __shfl_xor(ss, m, kWave);
+    ss = row_orbit_sum<TM>(ss);
+    ss += __shfl_xor(ss, 16, kWave);
+    ss += __shfl_xor(ss, 32, kWave);
     if (lane < TM) rb[PreLds<TM>::kRed + wave * TM + lane] = ss;
+    __syncthreads();
+    // per-token totals in a fixed order (waves, then ranges)
+    float* tot = rb + PreLds<TM>::kRed + PreLds<TM>::kSs;
+    if (tid < TM * 32) {
+      const int tk = tid / 32, c = tid % 32;
+      float a = 0.f;
+      if (c < kC4) {
+#pragma unroll
+        for (int w = 0; w < kMfmaWaves; ++w)
+#pragma unroll
+          for (int r = 0; r < R; ++r) a += rb[((w * R + r) * TM + tk) * 32 + c];
+      } else if (c == kC4) {
+#pragma unroll
+        for (int w = 0; w < kMfmaWaves; ++w) a += rb[PreLds<TM>::kRed + w * TM + tk];
+      }
+      tot[tid] = a;
+    }
     __syncthreads();
 
     // ---- 5. H_pre of this lane's token, then the collapse from registers
     float hpre[kN4];
     {
-      const float rstd = 1.0f / sqrtf(lds_ss<TM>(rb, tt) * rK + eps);
+      const float rstd = __builtin_amdgcn_rsqf(tot[tt * 32 + kC4] * rK + eps);
 #pragma unroll
-      for (int n = 0; n < kN4; ++n)
-        hpre[n] = sigmoid(a_pre * (rstd * lds_p<TM>(rb, tt, n)) + bias[n]);
+      for (int n = 0; n < kN4; ++n) hpre[n] = fast_sigmoid(a_pre * (rstd * tot[tt * 32 + n]) + bias_s[n]);
     }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -357,9 +396,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void hc_pre_mfma_kernel(
       }
       // add the other ranges' streams (lanes row ± TM·k in the same 16-lane row)
 #pragma unroll
-      for (int m = TM; m < 16; m <<= 1)
-#pragma unroll
-        for (int v = 0; v < 8; ++v) o[v] += __shfl_xor(o[v], m, kWave);
+      for (int v = 0; v < 8; ++v) o[v] = row_orbit_sum<TM>(o[v]);
       // range rr stores its 8/R share of the 8 d values
       constexpr int share = 8 / R;
       float sv[share];

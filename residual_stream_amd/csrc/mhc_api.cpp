@@ -8,7 +8,7 @@
 #include <cmath>
 #include <limits>
 
-#include "../../include/mhc.h"
+#include "mhc.h"
 #include "mhc_internal.h"
 
 namespace mhc {

@@ -5,7 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
-#include "../../include/mhc.h"
+#include "mhc.h"
 
 namespace mhc {
 
@@ -26,6 +26,15 @@ hipError_t launch_post_bwd(const mhc_desc& d, const void* dxn, const void* x, co
                            float* dH_post, float* dH_res, hipStream_t s);
 
 size_t pre_bwd_workspace_bytes(const mhc_desc& d);
+
+// Matrix-core backward of hc_pre (bf16, N = 4, D % 256 == 0); leaves the
+// per-token dℓ and dα terms in the workspace for the shared bias/α reduction.
+bool pre_bwd_mfma_eligible(const mhc_desc& d);
+size_t pre_bwd_mfma_workspace_bytes(const mhc_desc& d);
+hipError_t launch_pre_bwd_mfma(const mhc_desc& d, const void* dh, const void* x, const float* phi,
+                               const float* bias, const float* dH_post, const float* dH_res,
+                               void* dx, float* dphi, void* ws, float** dlog, float** dal,
+                               hipStream_t s);
 hipError_t launch_pre_bwd(const mhc_desc& d, const void* dh, const void* x, const float* phi,
                           const float* bias, const float* dH_post, const float* dH_res, void* dx,
                           float* dphi, float* dbias, float* dalpha, void* ws, hipStream_t s);

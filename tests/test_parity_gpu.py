@@ -91,6 +91,15 @@ def test_backward_shapes(io, N, T, D):
     check_backward(make_inputs(T, N, D, io=io, seed=100 + T + N + D, alpha=1.0, grads=True))
 
 
+@pytest.mark.parametrize("D", [256, 512, 2560])
+@pytest.mark.parametrize("T", [1, 5, 70, 300])
+@pytest.mark.parametrize("alpha", [0.01, 1.0])
+def test_backward_matrix_core_shapes(D, T, alpha):
+    # bf16 I/O, N = 4, D a multiple of 256: the split-K / per-slice matrix-core
+    # backward; token counts exercise partial tiles and partial token splits.
+    check_backward(make_inputs(T, 4, D, io="bf16", seed=7 * T + D, alpha=alpha, grads=True))
+
+
 @pytest.mark.parametrize("alpha", [0.01, 1.0])
 def test_tiny_workload_backward(alpha):
     check_backward(make_inputs(64, 4, 256, io="f32", seed=0, alpha=alpha, grads=True))
