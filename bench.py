@@ -54,6 +54,17 @@ def algo_bytes(T, N, D, io):
     }
 
 
+# Kernels each C-ABI call launches on the shapes timed here (N = 4, D = 5120,
+# bf16); the call's event time is the sum of their durations.
+CALL_KERNELS = {
+    "mhc_pre": ["phi_pack_kernel", "hc_pre_mfma_kernel"],
+    "mhc_post": ["hc_post_generic"],
+    "mhc_post_bwd": ["hc_post_bwd_generic"],
+    "mhc_pre_bwd": ["bwd_proj_kernel", "bwd_coef_kernel", "bwd_dx_kernel", "dphi_sum_kernel",
+                    "bias_alpha_reduce"],
+}
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "residual_stream_amd", "csrc")
@@ -110,6 +121,9 @@ def main():
     ap.add_argument("--workload", default="pro_s4096_bf16", choices=sorted(WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of one x-sized bf16 tensor (5 times), "
+                         "the reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -126,10 +140,20 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    mhc.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     T, N, D, io = WORKLOADS[args.workload]
+    if args.calibrate_copy:
+        n = T * N * D
+        a = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": 2 * n, "calibrate_copy_bytes_written": 2 * n,
+                          "launches": 5}))
+        return
+    mhc.load()
     K, C = N * D, N * N + 2 * N
     tdt = torch.bfloat16 if io == "bf16" else torch.float32
     kw = dict(iters=20, eps=1e-6, alphas=(0.01, 0.01, 0.01))
@@ -273,8 +297,10 @@ def main():
                     "gbps": fwd_bytes / (fwd_ms * 1e-3) / 1e9,
                     "frac_of_peak": fwd_bytes / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS},
         "per_call": per_call,
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
+        "roofline": {"kernel": dom, "kernels": CALL_KERNELS.get(dom, []), "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "algo_bytes_per_launch": ab[dom], "avg_us": per_call[dom]["avg_us"]},
         "kernel_source_hash": src_hash,
     }
     if not args.no_cpu_baseline:

@@ -31,8 +31,8 @@ constexpr int kN = 4;
 constexpr int kC = kN * kN + 2 * kN;  // 24
 constexpr int kPartStride = 32;       // floats per (slice, token): p[24], ss, dhp[4], pad
 constexpr int kSliceD = 256;          // d per projection slice (1024 k)
-constexpr int kProjThreads = 256;     // 4 waves × 16 tokens
-constexpr int kProjTokens = 256;      // tokens per projection workgroup
+constexpr int kProjThreads = 512;     // 8 waves × 16 tokens
+constexpr int kProjTokens = 128;      // tokens per projection workgroup
 
 __device__ __forceinline__ f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -54,17 +54,39 @@ __global__ __launch_bounds__(kProjThreads) void bwd_proj_kernel(
   const int K = kN * D;
   const int d_base = slice * kSliceD;
 
-  // φ slice → LDS (bf16, transposed)
-  for (int i = threadIdx.x; i < 4 * kSliceD * kC; i += kProjThreads) {
-    const int c = i % kC, kl = i / kC;
-    const int n = kl / kSliceD, dl = kl % kSliceD;
-    phiT[c * kPhiTRow + kl] = (uint16_t)f32_to_bf16_bits(phi[((int64_t)n * D + d_base + dl) * kC + c]);
+  // φ slice → LDS (bf16, transposed).  Each thread issues all its 16-byte
+  // loads first, then converts and stores: one L2 round trip, not dozens.
+  {
+    constexpr int kVec = 4 * kSliceD * kC / 4;               // float4 in the slice
+    constexpr int kPer = (kVec + kProjThreads - 1) / kProjThreads;
+    float4 v[kPer];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int i = threadIdx.x + r * kProjThreads;
+      if (i < kVec) {
+        const int kl = i / (kC / 4), c4 = i % (kC / 4);
+        const int n = kl / kSliceD, dl = kl % kSliceD;
+        v[r] = reinterpret_cast<const float4*>(phi + ((int64_t)n * D + d_base + dl) * kC)[c4];
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int i = threadIdx.x + r * kProjThreads;
+      if (i < kVec) {
+        const int kl = i / (kC / 4), c = 4 * (i % (kC / 4));
+        const uint32_t lo = pack_bf16x2(v[r].x, v[r].y), hi = pack_bf16x2(v[r].z, v[r].w);
+        phiT[(c + 0) * kPhiTRow + kl] = (uint16_t)(lo & 0xffffu);
+        phiT[(c + 1) * kPhiTRow + kl] = (uint16_t)(lo >> 16);
+        phiT[(c + 2) * kPhiTRow + kl] = (uint16_t)(hi & 0xffffu);
+        phiT[(c + 3) * kPhiTRow + kl] = (uint16_t)(hi >> 16);
+      }
+    }
   }
   __syncthreads();
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, g = lane >> 4;
-  for (int64_t t0 = tbeg + wave * 16; t0 < tbeg + kProjTokens && t0 < T; t0 += 64) {
+  for (int64_t t0 = tbeg + wave * 16; t0 < tbeg + kProjTokens && t0 < T; t0 += kProjThreads / 4) {
     const int64_t t = t0 + row;
     const bool tok = t < T;
     const int64_t tc = tok ? t : T - 1;  // clamp: rows past T load a valid row, results unused
@@ -264,144 +286,202 @@ __global__ __launch_bounds__(kCoefThreads) void bwd_coef_kernel(
     co[kC + 4 + i] = 0.f;
     if (i == 0) co[32] = rstd * rstd * rstd * dqp / (float)K;
     co[33 + i] = s_pre;
-    float* dl = dlog + t * kC;
-    dl[i] = dl_pre;
-    dl[kN + i] = dl_post;
+  }
+  // dbias and dα terms summed over the workgroup's 16 tokens (fixed butterfly
+  // order); tokens past T contribute zero.  One row per workgroup.
+  float red[2 * kN + 3] = {tok ? dl_pre : 0.f, tok ? dl_post : 0.f};
 #pragma unroll
-    for (int j = 0; j < kN; ++j) dl[2 * kN + i * kN + j] = dl_res[j];
-    if (i == 0) {
-      dal[t * 4 + 0] = da_pre;
-      dal[t * 4 + 1] = da_post;
-      dal[t * 4 + 2] = da_res;
-      dal[t * 4 + 3] = 0.f;
-    }
+  for (int j = 0; j < kN; ++j) red[2 + j] = tok ? dl_res[j] : 0.f;
+  red[6] = (tok && i == 0) ? da_pre : 0.f;
+  red[7] = (tok && i == 0) ? da_post : 0.f;
+  red[8] = (tok && i == 0) ? da_res : 0.f;
+#pragma unroll
+  for (int m = 4; m < 64; m <<= 1)
+#pragma unroll
+    for (int v = 0; v < 2 * kN + 3; ++v) red[v] += __shfl_xor(red[v], m, kWave);
+  if (lane < 4) {
+    float* dl = dlog + (int64_t)blockIdx.x * kC;
+    dl[i] = red[0];
+    dl[kN + i] = red[1];
+#pragma unroll
+    for (int j = 0; j < kN; ++j) dl[2 * kN + i * kN + j] = red[2 + j];
+  }
+  if (lane == 0) {
+    dal[(int64_t)blockIdx.x * 4 + 0] = red[6];
+    dal[(int64_t)blockIdx.x * 4 + 1] = red[7];
+    dal[(int64_t)blockIdx.x * 4 + 2] = red[8];
+    dal[(int64_t)blockIdx.x * 4 + 3] = 0.f;
   }
 }
 
 // ------------------------------------------------------------- pass 3 ---
-constexpr int kDxThreads = 256;  // 4 waves × 16 tokens
-constexpr int kDxK = 128;        // k per slice (32 d of each stream)
-constexpr int kDxTile = 64;      // tokens per tile
-constexpr int kPhiRow = 40;      // bf16 per φ row in LDS (32 + pad)
+// Workgroup = one k-slice (64 d of each stream, 256 k; 128-byte rows of every
+// token and stream) × a range of tokens, in tiles of 32 tokens.  Wave w takes
+// tokens 16·(w&1).. of the tile and the k-half w>>1 for dx, and k-blocks
+// 4w..4w+3 for dφ.  For dx the 16 A rows of a pair of MFMAs (blocks b = 0, 1)
+// are the φ rows k = 32p + 8·(r/4) + 4b + r%4, so the two results of a lane
+// cover 8 consecutive k (one 16-byte access of x, dh, dx).
+constexpr int kDxThreads = 256;
+constexpr int kDxK = 256;        // k per slice
+constexpr int kDxD = kDxK / kN;  // 64 d per stream
+constexpr int kDxTile = 32;      // tokens per tile
+constexpr int kPhiRow = 40;      // bf16 per φ row in LDS (32 c + pad)
 constexpr int kGRow = 40;        // bf16 per G row (32 c + pad)
-constexpr int kGTRow = 72;       // bf16 per Gᵀ row (64 t + pad)
-constexpr int kXTRow = 72;       // bf16 per xᵀ row (64 t + pad)
+constexpr int kTRow = 40;        // bf16 per Gᵀ / xᵀ row (32 t + pad)
 
 __global__ __launch_bounds__(kDxThreads) void bwd_dx_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ dh, const float* __restrict__ phi,
     const float* __restrict__ coef, uint16_t* __restrict__ dx, float* __restrict__ dphi_part,
     int64_t T, int D, int64_t tok_per_split) {
-  __shared__ uint16_t phis[kDxK * kPhiRow];     // φ[k][c], bf16
-  __shared__ uint16_t Gs[kDxTile * kGRow];      // G[t][c], bf16
-  __shared__ uint16_t GTs[32 * kGTRow];         // Gᵀ[c][t], bf16
-  __shared__ uint16_t xTs[kDxK * kXTRow];       // xᵀ[k][t], bf16
+  __shared__ uint16_t phis[kDxK * kPhiRow];  // φ[k][c]
+  __shared__ uint16_t Gs[kDxTile * kGRow];   // G[t][c]
+  __shared__ uint16_t GTs[32 * kTRow];       // Gᵀ[c][t]
+  __shared__ uint16_t xTs[kDxK * kTRow];     // xᵀ[k][t]
   __shared__ float betas[kDxTile];
   __shared__ float hps[kDxTile * kN];
 
   const int K = kN * D;
-  const int dpk = kDxK / kN;                      // 64 d per stream in this slice
-  const int sl = blockIdx.x;                      // k-slice: d in [sl·64, sl·64+64), all streams
-  const int d_base = sl * dpk;
+  const int d_base = blockIdx.x * kDxD;
   const int64_t tb = (int64_t)blockIdx.y * tok_per_split;
   int64_t te = tb + tok_per_split;
   if (te > T) te = T;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, g = lane >> 4;
 
-  // φ slice (k_local = n·64 + d_local) → LDS as bf16, c ≥ 24 zero
-  for (int i = threadIdx.x; i < kDxK * 32; i += kDxThreads) {
-    const int c = i & 31, kl = i >> 5;
-    const int n = kl / dpk, dl = kl % dpk;
-    float v = 0.f;
-    if (c < kC) v = phi[((int64_t)n * D + d_base + dl) * kC + c];
-    phis[kl * kPhiRow + c] = (uint16_t)f32_to_bf16_bits(v);
+  // φ slice (k_local = n·64 + d_local) → LDS as bf16 rows [k][c], c ≥ 24 zero;
+  // all loads of a thread in flight together
+  {
+    constexpr int kVec = kDxK * kC / 4;
+    constexpr int kPer = kVec / kDxThreads;
+    static_assert(kVec % kDxThreads == 0, "φ slice tiles the workgroup");
+    float4 v[kPer];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int i = threadIdx.x + r * kDxThreads;
+      const int kl = i / (kC / 4), c4 = i % (kC / 4);
+      const int n = kl / kDxD, dl = kl % kDxD;
+      v[r] = reinterpret_cast<const float4*>(phi + ((int64_t)n * D + d_base + dl) * kC)[c4];
+    }
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int i = threadIdx.x + r * kDxThreads;
+      const int kl = i / (kC / 4), c = 4 * (i % (kC / 4));
+      *reinterpret_cast<uint2*>(&phis[kl * kPhiRow + c]) =
+          make_uint2(pack_bf16x2(v[r].x, v[r].y), pack_bf16x2(v[r].z, v[r].w));
+    }
+    // zero columns 24..31
+    *reinterpret_cast<uint4*>(&phis[threadIdx.x * kPhiRow + kC]) = make_uint4(0, 0, 0, 0);
   }
 
-  // dφ accumulators: wave w owns k-blocks w and w+4 (16 k each) × 2 c-groups
-  constexpr int kKB = kDxK / 16 / 4;  // k-blocks per wave
-  f32x4_t dacc[kKB][2];
+  f32x4_t dacc[4][2];
 #pragma unroll
-  for (int a = 0; a < kKB; ++a) dacc[a][0] = dacc[a][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int a = 0; a < 4; ++a) dacc[a][0] = dacc[a][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int tl = (wave & 1) * 16 + row;  // this lane's token (D column) in the tile
+  const int khalf = wave >> 1;           // pairs 4·khalf .. 4·khalf+3 (32 k each)
+
+  // Per-tile token coefficients: thread i holds G[t][4·(i%8)..+3] of token
+  // t = t0 + i/8 (one float4), threads < 32 also β and H_pre.  Loaded one tile
+  // ahead so the staging never waits on a global round trip.
+  const int st_t = threadIdx.x >> 3, st_c = 4 * (threadIdx.x & 7);
+  auto fetch = [&](int64_t t0, float4& gv, float4& bh, float& be) {
+    const int64_t t = t0 + st_t;
+    gv = t < te ? *reinterpret_cast<const float4*>(coef + t * kCoefStride + st_c)
+                : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int64_t tb2 = t0 + threadIdx.x;
+    if (threadIdx.x < kDxTile && tb2 < te) {
+      be = coef[tb2 * kCoefStride + 32];
+      bh = *reinterpret_cast<const float4*>(coef + tb2 * kCoefStride + 33 - 1);  // [32..35]: β, H_pre 0..2
+      bh = make_float4(bh.y, bh.z, bh.w, coef[tb2 * kCoefStride + 36]);          // H_pre 0..3
+    } else {
+      be = 0.f;
+      bh = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  float4 n_gv, n_bh;
+  float n_be;
+  fetch(tb, n_gv, n_bh, n_be);
 
   for (int64_t t0 = tb; t0 < te; t0 += kDxTile) {
-    __syncthreads();  // previous tile's readers of Gs / GTs / xTs are done
-    // stage G (bf16, both orientations), β and H_pre of the tile's tokens
-    for (int i = threadIdx.x; i < kDxTile * 32; i += kDxThreads) {
-      const int tt = i >> 5, c = i & 31;
-      const int64_t t = t0 + tt;
-      const float gv = t < te ? coef[t * kCoefStride + c] : 0.f;
-      const uint16_t gb = (uint16_t)f32_to_bf16_bits(gv);
-      Gs[tt * kGRow + c] = gb;
-      GTs[c * kGTRow + tt] = gb;
-    }
-    if (threadIdx.x < kDxTile) {
-      const int64_t t = t0 + threadIdx.x;
-      betas[threadIdx.x] = t < te ? coef[t * kCoefStride + 32] : 0.f;
-#pragma unroll
-      for (int n = 0; n < kN; ++n) hps[threadIdx.x * kN + n] = t < te ? coef[t * kCoefStride + 33 + n] : 0.f;
+    __syncthreads();  // the previous tile's readers of Gs / GTs / xTs are done
+    {
+      const uint32_t lo = pack_bf16x2(n_gv.x, n_gv.y), hi = pack_bf16x2(n_gv.z, n_gv.w);
+      *reinterpret_cast<uint2*>(&Gs[st_t * kGRow + st_c]) = make_uint2(lo, hi);
+      GTs[(st_c + 0) * kTRow + st_t] = (uint16_t)(lo & 0xffffu);
+      GTs[(st_c + 1) * kTRow + st_t] = (uint16_t)(lo >> 16);
+      GTs[(st_c + 2) * kTRow + st_t] = (uint16_t)(hi & 0xffffu);
+      GTs[(st_c + 3) * kTRow + st_t] = (uint16_t)(hi >> 16);
+      if (threadIdx.x < kDxTile) {
+        betas[threadIdx.x] = n_be;
+        hps[threadIdx.x * kN + 0] = n_bh.x;
+        hps[threadIdx.x * kN + 1] = n_bh.y;
+        hps[threadIdx.x * kN + 2] = n_bh.z;
+        hps[threadIdx.x * kN + 3] = n_bh.w;
+      }
     }
     __syncthreads();
+    if (t0 + kDxTile < te) fetch(t0 + kDxTile, n_gv, n_bh, n_be);
 
-    // dx for this wave's 16 tokens, k-block by k-block
-    const int tl = wave * 16 + row;  // token (local) of this lane's D column
     const int64_t t = t0 + tl;
     const bool tok = t < te;
+    const int64_t tr = tok ? t : t0;
     const uint4 gb = *reinterpret_cast<const uint4*>(&Gs[tl * kGRow + 8 * g]);  // B: Gᵀ[c][t]
     const float beta = betas[tl];
 #pragma unroll
-    for (int kb = 0; kb < kDxK / 16; ++kb) {
-      // A: φ rows k = kb·16 + row, c = 8g..8g+7
-      const uint4 af = *reinterpret_cast<const uint4*>(&phis[(kb * 16 + row) * kPhiRow + 8 * g]);
-      const f32x4_t dxb = mfma(af, gb, f32x4_t{0.f, 0.f, 0.f, 0.f});
-      // this lane: k_local = kb·16 + 4g + q (q = 0..3), token tl
-      const int kl = kb * 16 + 4 * g;
-      const int n = kl / dpk, dl = kl % dpk;
-      const int64_t xo = (tok ? t : t0) * K + (int64_t)n * D + d_base + dl;
-      const int64_t ho = (tok ? t : t0) * D + d_base + dl;
-      const uint2 xv = *reinterpret_cast<const uint2*>(x + xo);
-      const uint2 hv = *reinterpret_cast<const uint2*>(dh + ho);
-      const uint2 dv = *reinterpret_cast<const uint2*>(dx + xo);
-      const float xf[4] = {bf16_lo(xv.x), bf16_hi(xv.x), bf16_lo(xv.y), bf16_hi(xv.y)};
-      const float hf[4] = {bf16_lo(hv.x), bf16_hi(hv.x), bf16_lo(hv.y), bf16_hi(hv.y)};
-      const float df[4] = {bf16_lo(dv.x), bf16_hi(dv.x), bf16_lo(dv.y), bf16_hi(dv.y)};
+    for (int pp = 0; pp < 4; ++pp) {
+      const int p = khalf * 4 + pp;  // 32-k pair index in the slice: stream p/2, d half p%2
+      const int n = p >> 1;
+      const int dl = (p & 1) * 32 + 8 * g;
+      const int64_t xo = tr * K + (int64_t)n * D + d_base + dl;
+      const uint4 xv = *reinterpret_cast<const uint4*>(x + xo);
+      const uint4 hv = *reinterpret_cast<const uint4*>(dh + tr * D + d_base + dl);
+      const uint4 dv = *reinterpret_cast<const uint4*>(dx + xo);
+      f32x4_t r[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int kr = 32 * p + 8 * (row >> 2) + 4 * b + (row & 3);  // A row → φ row
+        const uint4 af = *reinterpret_cast<const uint4*>(&phis[kr * kPhiRow + 8 * g]);
+        r[b] = mfma(af, gb, f32x4_t{0.f, 0.f, 0.f, 0.f});
+      }
+      const float dxb[8] = {r[0][0], r[0][1], r[0][2], r[0][3], r[1][0], r[1][1], r[1][2], r[1][3]};
       const float hp = hps[tl * kN + n];
-      float o[4];
+      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, hw[4] = {hv.x, hv.y, hv.z, hv.w},
+                     dw[4] = {dv.x, dv.y, dv.z, dv.w};
+      uint32_t ow[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = df[q] + dxb[q] - beta * xf[q] + hp * hf[q];
-      if (tok)
-        *reinterpret_cast<uint2*>(dx + xo) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-      // xᵀ tile for dφ (zeros for tokens past the range)
-      const uint16_t xb[4] = {(uint16_t)(xv.x & 0xffffu), (uint16_t)(xv.x >> 16),
-                              (uint16_t)(xv.y & 0xffffu), (uint16_t)(xv.y >> 16)};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) xTs[(kl + q) * kXTRow + tl] = tok ? xb[q] : (uint16_t)0;
+      for (int q = 0; q < 4; ++q) {
+        const float o0 = bf16_lo(dw[q]) + dxb[2 * q] - beta * bf16_lo(xw[q]) + hp * bf16_lo(hw[q]);
+        const float o1 = bf16_hi(dw[q]) + dxb[2 * q + 1] - beta * bf16_hi(xw[q]) + hp * bf16_hi(hw[q]);
+        ow[q] = pack_bf16x2(o0, o1);
+        // xᵀ for dφ; tokens past the range contribute zero
+        const int kl = 32 * p + 8 * g + 2 * q;
+        xTs[kl * kTRow + tl] = tok ? (uint16_t)(xw[q] & 0xffffu) : (uint16_t)0;
+        xTs[(kl + 1) * kTRow + tl] = tok ? (uint16_t)(xw[q] >> 16) : (uint16_t)0;
+      }
+      if (tok) *reinterpret_cast<uint4*>(dx + xo) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
     }
     __syncthreads();
 
-    // dφ[k][c] += Σ_t x[t][k]·G[t][c] over the tile: K-dim = 32 tokens per MFMA
+    // dφ[k][c] += Σ_t x[t][k]·G[t][c] over the 32 tokens of the tile
 #pragma unroll
-    for (int a = 0; a < kKB; ++a) {
-      const int kb = wave + 4 * a;
+    for (int a = 0; a < 4; ++a) {
+      const int kb = 4 * wave + a;
+      const uint4 af = *reinterpret_cast<const uint4*>(&xTs[(kb * 16 + row) * kTRow + 8 * g]);
 #pragma unroll
-      for (int ts = 0; ts < kDxTile / 32; ++ts) {
-        const uint4 af = *reinterpret_cast<const uint4*>(&xTs[(kb * 16 + row) * kXTRow + ts * 32 + 8 * g]);
-#pragma unroll
-        for (int cg = 0; cg < 2; ++cg) {
-          const uint4 bf = *reinterpret_cast<const uint4*>(&GTs[(cg * 16 + row) * kGTRow + ts * 32 + 8 * g]);
-          // A = xᵀ[k][t], B = G[t][c] read as Gᵀ[c][t]: lane holds column c = row, t = 8g..
-          dacc[a][cg] = mfma(af, bf, dacc[a][cg]);
-        }
+      for (int cg = 0; cg < 2; ++cg) {
+        const uint4 bf = *reinterpret_cast<const uint4*>(&GTs[(cg * 16 + row) * kTRow + 8 * g]);
+        dacc[a][cg] = mfma(af, bf, dacc[a][cg]);
       }
     }
   }
   // partial dφ of this (slice, token split): lane holds rows k = 4g+q, column c = row (+16)
 #pragma unroll
-  for (int a = 0; a < kKB; ++a) {
-    const int kb = wave + 4 * a;
+  for (int a = 0; a < 4; ++a) {
+    const int kb = 4 * wave + a;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int kl = kb * 16 + 4 * g + q;
-      const int n = kl / dpk, dl = kl % dpk;
+      const int n = kl / kDxD, dl = kl % kDxD;
       const int64_t k = (int64_t)n * D + d_base + dl;
       float* dst = dphi_part + ((int64_t)blockIdx.y * K + k) * kC;
       dst[row] = dacc[a][0][q];
@@ -431,7 +511,9 @@ static Layout layout(const mhc_desc& d) {
   Layout L;
   const size_t T = (size_t)d.T, K = (size_t)kN * d.D;
   L.S = d.D / kSliceD;
-  int64_t ts = (d.T + 1023) / 1024;
+  // token splits of the dx/dφ pass: enough workgroups to fill the chip
+  // (K/256 slices × TS), each split at least one 32-token tile
+  int64_t ts = (d.T + 511) / 512;
   L.TS = (int)(ts < 1 ? 1 : (ts > 8 ? 8 : ts));
   L.part = 0;
   L.coef = L.part + align256((size_t)L.S * T * kPartStride * 4);
@@ -462,7 +544,7 @@ hipError_t launch_pre_bwd_mfma(const mhc_desc& d, const void* dh, const void* x,
   float* dlog = reinterpret_cast<float*>(w + L.dlog);
   float* dal = reinterpret_cast<float*>(w + L.dal);
   float* dphi_part = reinterpret_cast<float*>(w + L.dphi);
-  *dlog_out = dlog;
+  *dlog_out = dlog;  // one row per 16 tokens
   *dal_out = dal;
   const int64_t T = d.T;
   const int K = kN * d.D;
@@ -476,7 +558,7 @@ hipError_t launch_pre_bwd_mfma(const mhc_desc& d, const void* dh, const void* x,
                      s, part, L.S, bias, dH_post, dH_res, coef, dlog, dal, T, d.D, d.sinkhorn_iters,
                      d.eps, d.alpha_pre, d.alpha_post, d.alpha_res);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int64_t tps = ((T + L.TS - 1) / L.TS + kDxTile - 1) / kDxTile * kDxTile;
+  const int64_t tps = ((T + L.TS - 1) / L.TS + kDxTile - 1) / kDxTile * kDxTile;  // tokens per split
   hipLaunchKernelGGL(bwd_dx_kernel, dim3((unsigned)(K / kDxK), (unsigned)L.TS), dim3(kDxThreads), 0, s,
                      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dh), phi, coef,
                      static_cast<uint16_t*>(dx), dphi_part, T, d.D, tps);
