@@ -29,15 +29,17 @@
  *     destination stream).
  *   - Alignment: every pointer 16-byte aligned.
  *   - Work is enqueued on `stream` and runs asynchronously; the library never
- *     allocates, frees or synchronises, and keeps no global state (calls are
- *     thread-safe).  Outputs are overwritten, except `dx` of mhc_pre_bwd,
+ *     allocates, frees or synchronises.  Its only global state is an atomic
+ *     per-call counter (calls are thread-safe).  A workspace must not be in
+ *     use by two calls at once.  Outputs are overwritten, except `dx` of mhc_pre_bwd,
  *     which is read-modify-write.
  *   - Errors: argument checks are synchronous and return a status without
  *     launching anything.  A failed launch returns MHC_ERR_HIP.  Device faults
  *     surface at the caller's next synchronisation, as in HIP.
  *   - Aliasing: outputs must not alias inputs (x_next ≠ x, y; dx ≠ dx_next).
  *   - Results are bitwise reproducible for the same inputs, shape and device
- *     (no atomics; reductions have a fixed order).
+ *     (reductions have a fixed order; atomics only order or hand out work,
+ *     they never accumulate values).
  */
 #ifndef MHC_H
 #define MHC_H
@@ -82,10 +84,14 @@ typedef struct mhc_desc {
  * for an invalid descriptor. */
 size_t mhc_pre_workspace_bytes(const mhc_desc* desc);
 
-/* hc_pre forward.  Reads x once per token tile, writes h[T][D] (I/O dtype) and
- * the fp32 coefficients H_pre, H_post, H_res.  `workspace` (may be NULL when
+/* hc_pre forward.  Reads x once, writes h[T][D] (I/O dtype) and the fp32
+ * coefficients H_pre, H_post, H_res.  `workspace` (may be NULL when
  * mhc_pre_workspace_bytes is 0) is scratch owned by the caller, at least
- * that many bytes, 256-byte aligned; its contents on entry are ignored. */
+ * that many bytes, 256-byte aligned; its contents on entry are ignored.  For
+ * bf16, N = 4, D = 5120 or 2560 the call splits each token's reduction across
+ * workgroups that exchange partial sums through the workspace, tagged per
+ * call, so two calls that share a workspace must not overlap in time (on one
+ * stream they never do). */
 mhc_status mhc_pre(const mhc_desc* desc, const void* x, const float* phi, const float* bias,
                    void* h, float* H_pre, float* H_post, float* H_res,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);

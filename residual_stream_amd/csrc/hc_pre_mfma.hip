@@ -471,7 +471,10 @@ static size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 size_t pre_workspace_bytes(const mhc_desc& d) {
   const PreConfig pc = pick_pre(d);
   if (pc.tm == 0) return 0;
-  return align256((size_t)pc.nsteps * pc.cg * pc.ps * 64 * sizeof(uint4));
+  const size_t own = align256((size_t)pc.nsteps * pc.cg * pc.ps * 64 * sizeof(uint4));
+  // the cooperative kernel may take the call instead; room for either
+  const size_t coop = pre_coop_eligible(d) ? pre_coop_workspace_bytes(d) : 0;
+  return own > coop ? own : coop;
 }
 
 hipError_t launch_pre_generic(const mhc_desc& d, const void* x, const float* phi,
@@ -503,6 +506,11 @@ hipError_t launch_pre(const mhc_desc& d, const void* x, const float* phi, const 
                       hipStream_t s) {
   const PreConfig pc = pick_pre(d);
   if (pc.tm == 0) return launch_pre_generic(d, x, phi, bias, h, H_pre, H_post, H_res, s);
+  if (pre_coop_eligible(d)) {
+    if (launch_pre_coop(d, x, phi, bias, h, H_pre, H_post, H_res, ws, s) == hipSuccess)
+      return hipSuccess;
+    (void)hipGetLastError();  // launch refused: clear the error and take the per-tile kernel
+  }
   if (d.io == kBF16) {
     if (pc.tm == 16) return launch_mfma<kBF16, 16, 10>(d, pc, x, phi, bias, h, H_pre, H_post, H_res, ws, s);
     return launch_mfma<kBF16, 8, 20>(d, pc, x, phi, bias, h, H_pre, H_post, H_res, ws, s);

@@ -1,6 +1,5 @@
 // C ABI of the mHC hot path (declared in include/mhc.h): argument validation
-// and dispatch to the gfx950 kernels.  No allocation, no synchronisation, no
-// global state.
+// and dispatch to the gfx950 kernels.  No allocation, no synchronisation.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -18,6 +18,14 @@ hipError_t launch_pre(const mhc_desc& d, const void* x, const float* phi, const 
                       void* h, float* H_pre, float* H_post, float* H_res, void* ws,
                       hipStream_t s);
 
+// Split-K hc_pre across workgroups (bf16, N = 4, D = 5120 or 2560): groups of
+// workgroups exchange partial sums through the workspace.
+bool pre_coop_eligible(const mhc_desc& d);
+size_t pre_coop_workspace_bytes(const mhc_desc& d);
+hipError_t launch_pre_coop(const mhc_desc& d, const void* x, const float* phi, const float* bias,
+                           void* h, float* H_pre, float* H_post, float* H_res, void* ws,
+                           hipStream_t s);
+
 hipError_t launch_post(const mhc_desc& d, const void* x, const void* y, const float* H_post,
                        const float* H_res, void* x_next, hipStream_t s);
 
