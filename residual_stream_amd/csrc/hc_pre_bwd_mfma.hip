@@ -34,6 +34,19 @@ constexpr int kSliceD = 256;          // d per projection slice (1024 k)
 constexpr int kProjThreads = 512;     // 8 waves × 16 tokens
 constexpr int kProjTokens = 128;      // tokens per projection workgroup
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint4 v) {
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{v.x, v.y, v.z, v.w}, r, (int)voff, 0, 0);
+}
+
 __device__ __forceinline__ f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
@@ -329,7 +342,7 @@ constexpr int kPhiRow = 40;      // bf16 per φ row in LDS (32 c + pad)
 constexpr int kGRow = 40;        // bf16 per G row (32 c + pad)
 constexpr int kTRow = 40;        // bf16 per Gᵀ / xᵀ row (32 t + pad)
 
-__global__ __launch_bounds__(kDxThreads) void bwd_dx_kernel(
+__global__ __launch_bounds__(kDxThreads, 2) void bwd_dx_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ dh, const float* __restrict__ phi,
     const float* __restrict__ coef, uint16_t* __restrict__ dx, float* __restrict__ dphi_part,
     int64_t T, int D, int64_t tok_per_split) {
@@ -384,58 +397,95 @@ __global__ __launch_bounds__(kDxThreads) void bwd_dx_kernel(
   // t = t0 + i/8 (one float4), threads < 32 also β and H_pre.  Loaded one tile
   // ahead so the staging never waits on a global round trip.
   const int st_t = threadIdx.x >> 3, st_c = 4 * (threadIdx.x & 7);
+  // Raw loads only (nothing computed from them here): a value built from a
+  // load would make this wave wait for it, and with it for every load issued
+  // before, i.e. the tile in flight.
   auto fetch = [&](int64_t t0, float4& gv, float4& bh, float& be) {
     const int64_t t = t0 + st_t;
-    gv = t < te ? *reinterpret_cast<const float4*>(coef + t * kCoefStride + st_c)
-                : make_float4(0.f, 0.f, 0.f, 0.f);
-    const int64_t tb2 = t0 + threadIdx.x;
-    if (threadIdx.x < kDxTile && tb2 < te) {
-      be = coef[tb2 * kCoefStride + 32];
-      bh = *reinterpret_cast<const float4*>(coef + tb2 * kCoefStride + 33 - 1);  // [32..35]: β, H_pre 0..2
-      bh = make_float4(bh.y, bh.z, bh.w, coef[tb2 * kCoefStride + 36]);          // H_pre 0..3
-    } else {
-      be = 0.f;
-      bh = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    const int64_t tr = t < te ? t : tb;  // a valid row; the values are not used
+    gv = *reinterpret_cast<const float4*>(coef + tr * kCoefStride + st_c);
+    const int64_t tb2 = t0 + (threadIdx.x & (kDxTile - 1));
+    const int64_t tr2 = tb2 < te ? tb2 : tb;
+    bh = *reinterpret_cast<const float4*>(coef + tr2 * kCoefStride + 32);  // β, H_pre 0..2
+    be = coef[tr2 * kCoefStride + 36];                                     // H_pre 3
   };
   float4 n_gv, n_bh;
   float n_be;
   fetch(tb, n_gv, n_bh, n_be);
 
-  for (int64_t t0 = tb; t0 < te; t0 += kDxTile) {
+  // x, dh and dx of a tile for this lane: pairs pp = 0..3 of its k-half.
+  // Two register buffers: the next tile's loads are in flight while the
+  // current one is computed and stored (vector memory completes in order, so
+  // those loads never wait on the stores issued after them).
+  // Buffer descriptors sized to the tile's rows inside the range: rows past
+  // it read zeros and their stores are dropped.  Per-lane offsets are the
+  // same for every tile.
+  // (pairs pp and pp + 2 cover the same d of two streams: one dh load each)
+  uint4 bx[2][4], bh[2][2], bd[2][4];
+  uint32_t vo_x[4], vo_h[2];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) {
+    const int p = khalf * 4 + pp;
+    const int dl = (p & 1) * 32 + 8 * g;
+    vo_x[pp] = (uint32_t)(((int64_t)tl * K + (int64_t)(p >> 1) * D + d_base + dl) * 2);
+    if (pp < 2) vo_h[pp] = (uint32_t)(((int64_t)tl * D + d_base + dl) * 2);
+  }
+  auto rows_in = [&](int64_t t0) -> uint32_t {
+    const int64_t r = te - t0;
+    return (uint32_t)(r <= 0 ? 0 : (r < kDxTile ? r : kDxTile));
+  };
+  auto load_tile = [&](int64_t t0, auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
+    const uint32_t rows = rows_in(t0);
+    const int64_t tbase = rows > 0 ? t0 : 0;
+    const auto rx = make_rsrc(x + tbase * K, rows * (uint32_t)K * 2);
+    const auto rh = make_rsrc(dh + tbase * D, rows * (uint32_t)D * 2);
+    const auto rd = make_rsrc(dx + tbase * K, rows * (uint32_t)K * 2);
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      bx[SL][pp] = ld16(rx, vo_x[pp]);
+      if (pp < 2) bh[SL][pp] = ld16(rh, vo_h[pp]);
+      bd[SL][pp] = ld16(rd, vo_x[pp]);
+    }
+  };
+
+  auto tile = [&](int64_t t0, auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
     __syncthreads();  // the previous tile's readers of Gs / GTs / xTs are done
     {
-      const uint32_t lo = pack_bf16x2(n_gv.x, n_gv.y), hi = pack_bf16x2(n_gv.z, n_gv.w);
+      // rows past the range get G = 0, β = 0, H_pre = 0
+      const bool in_g = t0 + st_t < te;
+      const float4 gv = in_g ? n_gv : make_float4(0.f, 0.f, 0.f, 0.f);
+      const uint32_t lo = pack_bf16x2(gv.x, gv.y), hi = pack_bf16x2(gv.z, gv.w);
       *reinterpret_cast<uint2*>(&Gs[st_t * kGRow + st_c]) = make_uint2(lo, hi);
       GTs[(st_c + 0) * kTRow + st_t] = (uint16_t)(lo & 0xffffu);
       GTs[(st_c + 1) * kTRow + st_t] = (uint16_t)(lo >> 16);
       GTs[(st_c + 2) * kTRow + st_t] = (uint16_t)(hi & 0xffffu);
       GTs[(st_c + 3) * kTRow + st_t] = (uint16_t)(hi >> 16);
       if (threadIdx.x < kDxTile) {
-        betas[threadIdx.x] = n_be;
-        hps[threadIdx.x * kN + 0] = n_bh.x;
-        hps[threadIdx.x * kN + 1] = n_bh.y;
-        hps[threadIdx.x * kN + 2] = n_bh.z;
-        hps[threadIdx.x * kN + 3] = n_bh.w;
+        const bool in_b = t0 + threadIdx.x < te;
+        betas[threadIdx.x] = in_b ? n_bh.x : 0.f;
+        hps[threadIdx.x * kN + 0] = in_b ? n_bh.y : 0.f;
+        hps[threadIdx.x * kN + 1] = in_b ? n_bh.z : 0.f;
+        hps[threadIdx.x * kN + 2] = in_b ? n_bh.w : 0.f;
+        hps[threadIdx.x * kN + 3] = in_b ? n_be : 0.f;
       }
     }
     __syncthreads();
-    if (t0 + kDxTile < te) fetch(t0 + kDxTile, n_gv, n_bh, n_be);
+    // next tile: coefficients and x / dh / dx into the other buffer
+    fetch(t0 + kDxTile, n_gv, n_bh, n_be);
+    load_tile(t0 + kDxTile, std::integral_constant<int, SL ^ 1>{});
 
     const int64_t t = t0 + tl;
     const bool tok = t < te;
-    const int64_t tr = tok ? t : t0;
+    const auto rd = make_rsrc(dx + t0 * K, rows_in(t0) * (uint32_t)K * 2);
     const uint4 gb = *reinterpret_cast<const uint4*>(&Gs[tl * kGRow + 8 * g]);  // B: Gᵀ[c][t]
     const float beta = betas[tl];
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {
       const int p = khalf * 4 + pp;  // 32-k pair index in the slice: stream p/2, d half p%2
       const int n = p >> 1;
-      const int dl = (p & 1) * 32 + 8 * g;
-      const int64_t xo = tr * K + (int64_t)n * D + d_base + dl;
-      const uint4 xv = *reinterpret_cast<const uint4*>(x + xo);
-      const uint4 hv = *reinterpret_cast<const uint4*>(dh + tr * D + d_base + dl);
-      const uint4 dv = *reinterpret_cast<const uint4*>(dx + xo);
+      const uint4 xv = bx[SL][pp], hv = bh[SL][pp & 1], dv = bd[SL][pp];
       f32x4_t r[2];
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
@@ -458,7 +508,7 @@ __global__ __launch_bounds__(kDxThreads) void bwd_dx_kernel(
         xTs[kl * kTRow + tl] = tok ? (uint16_t)(xw[q] & 0xffffu) : (uint16_t)0;
         xTs[(kl + 1) * kTRow + tl] = tok ? (uint16_t)(xw[q] >> 16) : (uint16_t)0;
       }
-      if (tok) *reinterpret_cast<uint4*>(dx + xo) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+      st16(rd, vo_x[pp], make_uint4(ow[0], ow[1], ow[2], ow[3]));
     }
     __syncthreads();
 
@@ -473,6 +523,13 @@ __global__ __launch_bounds__(kDxThreads) void bwd_dx_kernel(
         dacc[a][cg] = mfma(af, bf, dacc[a][cg]);
       }
     }
+  };
+
+  load_tile(tb, std::integral_constant<int, 0>{});
+  for (int64_t t0 = tb; t0 < te; t0 += 2 * kDxTile) {
+    tile(t0, std::integral_constant<int, 0>{});
+    if (t0 + kDxTile >= te) break;
+    tile(t0 + kDxTile, std::integral_constant<int, 1>{});
   }
   // partial dφ of this (slice, token split): lane holds rows k = 4g+q, column c = row (+16)
 #pragma unroll
@@ -511,9 +568,13 @@ static Layout layout(const mhc_desc& d) {
   Layout L;
   const size_t T = (size_t)d.T, K = (size_t)kN * d.D;
   L.S = d.D / kSliceD;
-  // token splits of the dx/dφ pass: enough workgroups to fill the chip
-  // (K/256 slices × TS), each split at least one 32-token tile
-  int64_t ts = (d.T + 511) / 512;
+  // token splits of the dx/dφ pass: about two workgroups per CU of a
+  // 256-CU chip (K/256 slices × TS ≤ 512, two resident per CU), at most one
+  // split per 32-token tile
+  const int64_t nsl = (int64_t)K / kDxK;
+  int64_t ts = 512 / nsl;
+  const int64_t tiles = (d.T + kDxTile - 1) / kDxTile;
+  if (ts > tiles) ts = tiles;
   L.TS = (int)(ts < 1 ? 1 : (ts > 8 ? 8 : ts));
   L.part = 0;
   L.coef = L.part + align256((size_t)L.S * T * kPartStride * 4);
