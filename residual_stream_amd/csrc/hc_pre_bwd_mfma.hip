@@ -4,10 +4,10 @@
 // forward recomputed from x (Ascend mHC Triton article, intra-layer recompute
 // paragraph).  Three passes:
 //
-//  1. bwd_proj_kernel — split-K reduction.  A workgroup keeps one d-slice of φ
-//     (all four streams) in LDS as bf16 and streams x and dh for a range of
-//     tokens: per (token, slice) it writes the raw projections x·φ (matrix
-//     cores), the sum of squares and <dh, x[n]> (vector ALU).
+//  1. bwd_proj_kernel — split-K reduction.  A persistent workgroup keeps one
+//     d-slice of φ (all four streams) in registers as bf16 and streams x and
+//     dh for a contiguous token range: per (token, slice) it writes the raw
+//     projections x·φ (matrix cores), the sum of squares and <dh, x[n]>.
 //  2. bwd_coef_kernel — per token, four lanes (one per H_res row): sums the
 //     slices, recomputes rstd, logits, gates and the Sinkhorn rounds (keeping
 //     the row/column scalings u, v of every round in LDS), walks the rounds
@@ -30,9 +30,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kN = 4;
 constexpr int kC = kN * kN + 2 * kN;  // 24
 constexpr int kPartStride = 32;       // floats per (slice, token): p[24], ss, dhp[4], pad
-constexpr int kSliceD = 256;          // d per projection slice (1024 k)
-constexpr int kProjThreads = 512;     // 8 waves × 16 tokens
-constexpr int kProjTokens = 128;      // tokens per projection workgroup
+constexpr int kSliceD = 256;          // granularity of D for this path
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -53,98 +51,138 @@ __device__ __forceinline__ f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
 }
 
 // ------------------------------------------------------------- pass 1 ---
-// LDS φ slice, transposed: phiT[c][k] (c < 32, k < 1024 of the slice; the k
-// order is stream-major, k_local = n·256 + d_local), rows padded by 8 bf16.
-constexpr int kPhiTRow = 4 * kSliceD + 8;  // 24 rows of c: 49.5 KB
+// Persistent split-K reduction.  A workgroup = W waves, each owning one 32-d
+// block (all four streams) of a slice of 32·W d, walks a contiguous token range
+// in 16-token blocks.  Its φ B fragments stay in VGPRs; x and dh stream three
+// blocks ahead (a ring of four register slots, loaded through row-bounded
+// buffer descriptors); the projections go to the matrix cores, the sums of
+// squares and <dh, x[n]> to v_dot2_f32_bf16.  The waves' partials meet in LDS
+// (double-buffered, one barrier per block) and one summed record per (slice,
+// token) goes to the workspace.
+constexpr int kPRing = 4;    // register slots of x/dh per wave
+constexpr int kPRec = 29;    // record: p[24], ss, dhp[4]
 
-__global__ __launch_bounds__(kProjThreads) void bwd_proj_kernel(
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, true));
+}
+// Σ of the products of the two bf16 pairs in a and b, added to c.
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b),
+                                         c, false);
+}
+
+template <int W>
+__global__ __launch_bounds__(64 * W, 1) void bwd_proj_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ dh, const float* __restrict__ phi,
-    float* __restrict__ part, int64_t T, int D) {
-  __shared__ uint16_t phiT[kC * kPhiTRow];
+    float* __restrict__ part, int64_t T, int D, int64_t R) {
+  constexpr int kThr = 64 * W;
+  constexpr int kSl = 32 * W;  // d per slice
+  __shared__ __align__(16) float red[2][W][16][kPartStride];
+  // Token indices are 32-bit (T < 2^31): uniform compares then stay scalar,
+  // and no VGPR temporary (which could alias an in-flight load) is needed.
   const int slice = blockIdx.x;
-  const int nslices = gridDim.x;
-  const int64_t tbeg = (int64_t)blockIdx.y * kProjTokens;
+  const int tb = (int)(blockIdx.y * R);
+  const int te = (int64_t)tb + R < T ? tb + (int)R : (int)T;
+  const int nblk = te > tb ? (te - tb + 15) / 16 : 0;
   const int K = kN * D;
-  const int d_base = slice * kSliceD;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int row = lane & 15, g = lane >> 4;
+  const int d0 = slice * kSl + wave * 32;  // this wave's d block
 
-  // φ slice → LDS (bf16, transposed).  Each thread issues all its 16-byte
-  // loads first, then converts and stores: one L2 round trip, not dozens.
+  uint4 xs[kPRing][kN], hs[kPRing];
+  auto load_blk = [&](int b, auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
+    const int t0 = tb + 16 * b;
+    const int rows = b < nblk ? ((te - t0) < 16 ? (te - t0) : 16) : 0;
+    const int base = rows > 0 ? t0 : 0;
+    const auto rx = make_rsrc(x + (int64_t)base * K, (uint32_t)rows * (uint32_t)K * 2u);
+    const auto rh = make_rsrc(dh + (int64_t)base * D, (uint32_t)rows * (uint32_t)D * 2u);
+#pragma unroll
+    for (int n = 0; n < kN; ++n) xs[SL][n] = ld16(rx, (uint32_t)(((row * kN + n) * D + d0 + 8 * g) * 2));
+    hs[SL] = ld16(rh, (uint32_t)((row * D + d0 + 8 * g) * 2));
+  };
+
+  // φ: stream by stream through LDS (the red buffer), all global loads of a
+  // thread issued before the first LDS write
+  uint4 bfr[kN][2];
   {
-    constexpr int kVec = 4 * kSliceD * kC / 4;               // float4 in the slice
-    constexpr int kPer = (kVec + kProjThreads - 1) / kProjThreads;
-    float4 v[kPer];
+    constexpr int kV4 = kSl * kC / 4;  // float4 of one stream's slice rows
+    constexpr int kPer = (kV4 + kThr - 1) / kThr;
+    float4 f[kN][kPer];
 #pragma unroll
-    for (int r = 0; r < kPer; ++r) {
-      const int i = threadIdx.x + r * kProjThreads;
-      if (i < kVec) {
-        const int kl = i / (kC / 4), c4 = i % (kC / 4);
-        const int n = kl / kSliceD, dl = kl % kSliceD;
-        v[r] = reinterpret_cast<const float4*>(phi + ((int64_t)n * D + d_base + dl) * kC)[c4];
-      }
-    }
+    for (int n = 0; n < kN; ++n)
 #pragma unroll
-    for (int r = 0; r < kPer; ++r) {
-      const int i = threadIdx.x + r * kProjThreads;
-      if (i < kVec) {
-        const int kl = i / (kC / 4), c = 4 * (i % (kC / 4));
-        const uint32_t lo = pack_bf16x2(v[r].x, v[r].y), hi = pack_bf16x2(v[r].z, v[r].w);
-        phiT[(c + 0) * kPhiTRow + kl] = (uint16_t)(lo & 0xffffu);
-        phiT[(c + 1) * kPhiTRow + kl] = (uint16_t)(lo >> 16);
-        phiT[(c + 2) * kPhiTRow + kl] = (uint16_t)(hi & 0xffffu);
-        phiT[(c + 3) * kPhiTRow + kl] = (uint16_t)(hi >> 16);
+      for (int k = 0; k < kPer; ++k) {
+        const int i = threadIdx.x + k * kThr;
+        f[n][k] = i < kV4 ? reinterpret_cast<const float4*>(phi + ((int64_t)n * D + slice * kSl) * kC)[i]
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
       }
+    float* stage = &red[0][0][0][0];
+    static_assert(kSl * kC <= 2 * W * 16 * kPartStride, "one stream's φ slice fits the red buffer");
+#pragma unroll
+    for (int n = 0; n < kN; ++n) {
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int i = threadIdx.x + k * kThr;
+        if (i < kV4) reinterpret_cast<float4*>(stage)[i] = f[n][k];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int cg = 0; cg < 2; ++cg) {
+        const int c = cg * 16 + row;
+        float v8[8];
+#pragma unroll
+        for (int v = 0; v < 8; ++v) v8[v] = c < kC ? stage[(wave * 32 + 8 * g + v) * kC + c] : 0.f;
+        bfr[n][cg] = make_uint4(pack_bf16x2(v8[0], v8[1]), pack_bf16x2(v8[2], v8[3]),
+                                pack_bf16x2(v8[4], v8[5]), pack_bf16x2(v8[6], v8[7]));
+      }
+      __syncthreads();
     }
   }
-  __syncthreads();
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row = lane & 15, g = lane >> 4;
-  for (int64_t t0 = tbeg + wave * 16; t0 < tbeg + kProjTokens && t0 < T; t0 += kProjThreads / 4) {
-    const int64_t t = t0 + row;
-    const bool tok = t < T;
-    const int64_t tc = tok ? t : T - 1;  // clamp: rows past T load a valid row, results unused
-    const uint16_t* xr = x + tc * K;
-    const uint16_t* dr = dh + tc * D;
+  // the first blocks go out after φ, so that the wait counts at the top of
+  // the block loop are the same on entry and on every later pass
+  // (kept in issue order: the wait counts in the loop assume slot 0 oldest)
+  load_blk(0, std::integral_constant<int, 0>{});
+  __builtin_amdgcn_sched_barrier(0);
+  load_blk(1, std::integral_constant<int, 1>{});
+  __builtin_amdgcn_sched_barrier(0);
+  load_blk(2, std::integral_constant<int, 2>{});
+  __builtin_amdgcn_sched_barrier(0);
+
+  auto block = [&](int b, auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
+    load_blk(b + kPRing - 1, std::integral_constant<int, (SL + kPRing - 1) % kPRing>{});
+    __builtin_amdgcn_sched_barrier(0);
     f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     float ss = 0.f, dhp[kN] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-    for (int db = 0; db < kSliceD / 32; ++db) {
-      const int d0 = d_base + db * 32 + 8 * g;
-      const uint4 hv = *reinterpret_cast<const uint4*>(dr + d0);
-      uint4 xv[kN];
+    const uint4 hv = hs[SL];
 #pragma unroll
-      for (int n = 0; n < kN; ++n) xv[n] = *reinterpret_cast<const uint4*>(xr + (int64_t)n * D + d0);
-      const float hf[8] = {bf16_lo(hv.x), bf16_hi(hv.x), bf16_lo(hv.y), bf16_hi(hv.y),
-                           bf16_lo(hv.z), bf16_hi(hv.z), bf16_lo(hv.w), bf16_hi(hv.w)};
-#pragma unroll
-      for (int n = 0; n < kN; ++n) {
-        const int kl = n * kSliceD + db * 32 + 8 * g;
-        const uint4 b0 = *reinterpret_cast<const uint4*>(&phiT[row * kPhiTRow + kl]);
-        // columns 24..31 of the second group are zero
-        uint4 b1 = *reinterpret_cast<const uint4*>(&phiT[(16 + (row & 7)) * kPhiTRow + kl]);
-        if (row >= kC - 16) b1 = make_uint4(0, 0, 0, 0);
-        acc0 = mfma(xv[n], b0, acc0);
-        acc1 = mfma(xv[n], b1, acc1);
-        const float xf[8] = {bf16_lo(xv[n].x), bf16_hi(xv[n].x), bf16_lo(xv[n].y), bf16_hi(xv[n].y),
-                             bf16_lo(xv[n].z), bf16_hi(xv[n].z), bf16_lo(xv[n].w), bf16_hi(xv[n].w)};
-#pragma unroll
-        for (int v = 0; v < 8; ++v) {
-          ss += xf[v] * xf[v];
-          dhp[n] += hf[v] * xf[v];
-        }
-      }
+    for (int n = 0; n < kN; ++n) {
+      const uint4 a = xs[SL][n];
+      acc0 = mfma(a, bfr[n][0], acc0);
+      acc1 = mfma(a, bfr[n][1], acc1);
+      ss = dot2(a.x, a.x, ss);
+      ss = dot2(a.y, a.y, ss);
+      ss = dot2(a.z, a.z, ss);
+      ss = dot2(a.w, a.w, ss);
+      dhp[n] = dot2(a.x, hv.x, dhp[n]);
+      dhp[n] = dot2(a.y, hv.y, dhp[n]);
+      dhp[n] = dot2(a.z, hv.z, dhp[n]);
+      dhp[n] = dot2(a.w, hv.w, dhp[n]);
     }
-    // raw projections: lane holds rows (tokens) 4g..4g+3 of column `row` (+16)
-    float* pbase = part + ((int64_t)slice * T) * kPartStride;
+    float(*rw)[kPartStride] = red[b & 1][wave];
+    // D layout: lane holds tokens 4g+q of logit column row (+16)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int64_t tq = t0 + 4 * g + q;
-      if (tq < T) {
-        pbase[tq * kPartStride + row] = acc0[q];
-        if (row < kC - 16) pbase[tq * kPartStride + 16 + row] = acc1[q];
-      }
+      rw[4 * g + q][row] = acc0[q];
+      if (row < kC - 16) rw[4 * g + q][16 + row] = acc1[q];
     }
-    // sum of squares and <dh, x[n]>: reduce over the four k-groups of a token
+    // sums over the four k-groups of a token (lanes row + 16g)
     ss += __shfl_xor(ss, 16, kWave);
     ss += __shfl_xor(ss, 32, kWave);
 #pragma unroll
@@ -152,13 +190,38 @@ __global__ __launch_bounds__(kProjThreads) void bwd_proj_kernel(
       dhp[n] += __shfl_xor(dhp[n], 16, kWave);
       dhp[n] += __shfl_xor(dhp[n], 32, kWave);
     }
-    if (g == 0 && tok) {
-      pbase[t * kPartStride + kC] = ss;
+    if (g == 0) {
+      rw[row][kC] = ss;
 #pragma unroll
-      for (int n = 0; n < kN; ++n) pbase[t * kPartStride + kC + 1 + n] = dhp[n];
+      for (int n = 0; n < kN; ++n) rw[row][kC + 1 + n] = dhp[n];
     }
+    __syncthreads();
+    // record of each token: the W waves summed in a fixed order; rows past
+    // the range fall outside the store descriptor
+    const int t0 = tb + 16 * b;
+    const int rows = b < nblk ? ((te - t0) < 16 ? (te - t0) : 16) : 0;
+    const auto rp = make_rsrc(part + ((int64_t)slice * T + (rows > 0 ? t0 : 0)) * kPartStride,
+                              (uint32_t)rows * kPartStride * 4u);
+    static_assert(16 * kPRec <= kThr, "one record value per thread");
+    if (threadIdx.x < 16 * kPRec) {
+      const int tk = threadIdx.x / kPRec, c = threadIdx.x % kPRec;
+      float v = red[b & 1][0][tk][c];
+#pragma unroll
+      for (int w = 1; w < W; ++w) v += red[b & 1][w][tk][c];
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rp, (tk * kPartStride + c) * 4, 0, 0);
+    }
+  };
+
+  // Whole ring turns only (blocks past the range load and store nothing): a
+  // loop with a single exit keeps each slot in the same registers on every
+  // pass, so the wait counts stay exact across the back edge.
+  static_assert(kPRing == 4, "unroll below");
+  for (int b = 0; b < nblk; b += kPRing) {
+    block(b, std::integral_constant<int, 0>{});
+    block(b + 1, std::integral_constant<int, 1>{});
+    block(b + 2, std::integral_constant<int, 2>{});
+    block(b + 3, std::integral_constant<int, 3>{});
   }
-  (void)nslices;
 }
 
 // ------------------------------------------------------------- pass 2 ---
@@ -167,11 +230,6 @@ __global__ __launch_bounds__(kProjThreads) void bwd_proj_kernel(
 constexpr int kCoefStride = 64;
 constexpr int kCoefThreads = 64;  // 16 tokens × 4 rows
 
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
-                                                               0xF, 0xF, true));
-}
 constexpr int kQuadXor1 = 0xB1;
 constexpr int kQuadXor2 = 0x4E;
 __device__ __forceinline__ float quad_sum(float v) {
@@ -525,10 +583,14 @@ __global__ __launch_bounds__(kDxThreads, 2) void bwd_dx_kernel(
     }
   };
 
+  __builtin_amdgcn_sched_barrier(0);
   load_tile(tb, std::integral_constant<int, 0>{});
+  __builtin_amdgcn_sched_barrier(0);
+  // Whole pairs of tiles only (a tile past the range loads and stores
+  // nothing and adds zero to dφ): a loop with a single exit keeps each buffer
+  // in the same registers on every pass, so the wait counts stay exact.
   for (int64_t t0 = tb; t0 < te; t0 += 2 * kDxTile) {
     tile(t0, std::integral_constant<int, 0>{});
-    if (t0 + kDxTile >= te) break;
     tile(t0 + kDxTile, std::integral_constant<int, 1>{});
   }
   // partial dφ of this (slice, token split): lane holds rows k = 4g+q, column c = row (+16)
@@ -560,14 +622,24 @@ __global__ __launch_bounds__(256) void dphi_sum_kernel(const float* __restrict__
 static size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 struct Layout {
-  int S, TS;
+  int W, S, PS, TS;   // projection: waves per workgroup, slices, token splits; dx: token splits
+  int64_t R;          // projection tokens per split
   size_t part, coef, dlog, dal, dphi, total;
 };
 
 static Layout layout(const mhc_desc& d) {
   Layout L;
   const size_t T = (size_t)d.T, K = (size_t)kN * d.D;
-  L.S = d.D / kSliceD;
+  // projection slices of 320 d (ten waves) when D allows, else 256 d (eight);
+  // about one workgroup per CU of a 256-CU chip, whole 16-token blocks
+  L.W = d.D % 320 == 0 ? 10 : 8;
+  L.S = d.D / (32 * L.W);
+  const int64_t blocks = (d.T + 15) / 16;
+  int64_t ps = 256 / L.S;
+  if (ps > blocks) ps = blocks;
+  if (ps < 1) ps = 1;
+  L.R = (blocks + ps - 1) / ps * 16;
+  L.PS = (int)((d.T + L.R - 1) / L.R);
   // token splits of the dx/dφ pass: about two workgroups per CU of a
   // 256-CU chip (K/256 slices × TS ≤ 512, two resident per CU), at most one
   // split per 32-token tile
@@ -609,9 +681,13 @@ hipError_t launch_pre_bwd_mfma(const mhc_desc& d, const void* dh, const void* x,
   *dal_out = dal;
   const int64_t T = d.T;
   const int K = kN * d.D;
-  hipLaunchKernelGGL(bwd_proj_kernel, dim3((unsigned)L.S, (unsigned)((T + kProjTokens - 1) / kProjTokens)),
-                     dim3(kProjThreads), 0, s, static_cast<const uint16_t*>(x),
-                     static_cast<const uint16_t*>(dh), phi, part, T, d.D);
+  const dim3 pgrid((unsigned)L.S, (unsigned)L.PS);
+  if (L.W == 10)
+    hipLaunchKernelGGL(bwd_proj_kernel<10>, pgrid, dim3(640), 0, s, static_cast<const uint16_t*>(x),
+                       static_cast<const uint16_t*>(dh), phi, part, T, d.D, L.R);
+  else
+    hipLaunchKernelGGL(bwd_proj_kernel<8>, pgrid, dim3(512), 0, s, static_cast<const uint16_t*>(x),
+                       static_cast<const uint16_t*>(dh), phi, part, T, d.D, L.R);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t hist_bytes = (size_t)d.sinkhorn_iters * 2 * 64 * sizeof(float);

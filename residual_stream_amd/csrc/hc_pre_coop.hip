@@ -175,7 +175,10 @@ __global__ __launch_bounds__(kThreads, 1) void hc_pre_coop_kernel(
   constexpr float rK = 1.0f / (float)K;
   const int64_t ntiles = (T + kTM - 1) / kTM;
   const int64_t nloc = grp < ntiles ? (ntiles - grp + Q - 1) / Q : 0;  // this group's tiles
-  const int64_t nper = nloc + kLag;                                       // periods
+  // periods: a whole number of turns of the compute waves' register ring
+  // (periods past the last collapse do nothing), so that their loop has a
+  // single exit and keeps each slot in the same registers on every pass
+  const int64_t nper = (nloc + kLag + kSlots - 1) / kSlots * kSlots;
   auto tile_of = [&](int64_t p) { return grp + p * Q; };
   auto rows_of = [&](int64_t p) -> int64_t {  // valid tokens of the group's p-th tile
     if (p < 0 || p >= nloc) return 0;
@@ -243,7 +246,9 @@ __global__ __launch_bounds__(kThreads, 1) void hc_pre_coop_kernel(
   };
   static_assert(kAhead == 2, "prologue below issues two tiles");
   stage_phi([&]() {
+    // kept in issue order: the wait counts in the loop assume slot 0 oldest
     load_tile(0, std::integral_constant<int, 0>{});
+    __builtin_amdgcn_sched_barrier(0);
     load_tile(1, std::integral_constant<int, 1>{});
   });
   // the slots of tiles before the first are collapsed into dropped stores
@@ -317,17 +322,11 @@ __global__ __launch_bounds__(kThreads, 1) void hc_pre_coop_kernel(
     static_assert(kSlots == 7, "unroll below");
     for (int64_t p = 0; p < nper; p += kSlots) {
       period(p, std::integral_constant<int, 0>{});
-      if (p + 1 >= nper) break;
       period(p + 1, std::integral_constant<int, 1>{});
-      if (p + 2 >= nper) break;
       period(p + 2, std::integral_constant<int, 2>{});
-      if (p + 3 >= nper) break;
       period(p + 3, std::integral_constant<int, 3>{});
-      if (p + 4 >= nper) break;
       period(p + 4, std::integral_constant<int, 4>{});
-      if (p + 5 >= nper) break;
       period(p + 5, std::integral_constant<int, 5>{});
-      if (p + 6 >= nper) break;
       period(p + 6, std::integral_constant<int, 6>{});
     }
   } else {
