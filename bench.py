@@ -57,7 +57,7 @@ def algo_bytes(T, N, D, io):
 # Kernels each C-ABI call launches on the shapes timed here (N = 4, D = 5120,
 # bf16); the call's event time is the sum of their durations.
 CALL_KERNELS = {
-    "mhc_pre": ["phi_pack_kernel", "hc_pre_mfma_kernel"],
+    "mhc_pre": ["hc_pre_coop_kernel"],
     "mhc_post": ["hc_post_generic"],
     "mhc_post_bwd": ["hc_post_bwd_generic"],
     "mhc_pre_bwd": ["bwd_proj_kernel", "bwd_coef_kernel", "bwd_dx_kernel", "dphi_sum_kernel",
