@@ -60,8 +60,7 @@ CALL_KERNELS = {
     "mhc_pre": ["hc_pre_coop_kernel"],
     "mhc_post": ["hc_post_generic"],
     "mhc_post_bwd": ["hc_post_bwd_generic"],
-    "mhc_pre_bwd": ["bwd_proj_kernel", "bwd_coef_kernel", "bwd_dx_kernel", "dphi_sum_kernel",
-                    "bias_alpha_reduce"],
+    "mhc_pre_bwd": ["bwd_proj_kernel", "bwd_coef_kernel", "bwd_dx_kernel", "dphi_bias_sum_kernel"],
 }
 
 

@@ -366,13 +366,7 @@ hipError_t launch_pre_bwd(const mhc_desc& d, const void* dh, const void* x, cons
                           const float* bias, const float* dH_post, const float* dH_res, void* dx,
                           float* dphi, float* dbias, float* dalpha, void* ws, hipStream_t s) {
   if (pre_bwd_mfma_eligible(d)) {
-    float *dlog = nullptr, *dal = nullptr;
-    hipError_t e = launch_pre_bwd_mfma(d, dh, x, phi, bias, dH_post, dH_res, dx, dphi, ws, &dlog, &dal, s);
-    if (e != hipSuccess) return e;
-    // the matrix-core path leaves one pre-summed row per 16 tokens
-    hipLaunchKernelGGL((bias_alpha_reduce<4>), dim3(1), dim3(kBwdThreads), 0, s, dlog, dal, dbias, dalpha,
-                       (int64_t)((d.T + 15) / 16));
-    return hipGetLastError();
+    return launch_pre_bwd_mfma(d, dh, x, phi, bias, dH_post, dH_res, dx, dphi, dbias, dalpha, ws, s);
   }
   const PreBwdLayout L = pre_bwd_layout(d);
   char* w = static_cast<char*>(ws);

@@ -16,8 +16,8 @@
 //  3. bwd_dx_kernel — per k-slice: dx += G·φᵀ − β·x + H_pre[n]·dh (matrix
 //     cores, φ slice in LDS) and the partial dφ = Σ_t x_tᵀ G_t over its token
 //     range (matrix cores on an LDS-transposed copy of the x tile).
-// A final kernel sums the dφ partials (fixed order); dbias / dα reuse the
-// generic reductions.
+// A final kernel sums the dφ partials and the per-16-token dbias / dα rows
+// (fixed orders).
 #include "mhc_coef.h"
 #include "mhc_internal.h"
 
@@ -252,20 +252,46 @@ __global__ __launch_bounds__(kCoefThreads) void bwd_coef_kernel(
 
   // slice sums (fixed order) of this row's columns: pre i, post i, res row i, ss, dhp i
   float p_pre = 0.f, p_post = 0.f, p_res[kN] = {0.f, 0.f, 0.f, 0.f}, ss = 0.f, dhp = 0.f;
-  for (int s = 0; s < nslices; ++s) {
-    const float* pp = part + ((int64_t)s * T + tc) * kPartStride;
-    p_pre += pp[i];
-    p_post += pp[kN + i];
+  // eight slices' loads in flight at once (one memory round trip per eight
+  // slices instead of one per slice); slices past the count read slice 0 and
+  // add nothing, so the sums keep the slice order
+  constexpr int kChunk = 8;
+  for (int s0 = 0; s0 < nslices; s0 += kChunk) {
+    float4 va[kChunk], vb[kChunk];
+    float vc[kChunk], vd[kChunk], ve[kChunk];
 #pragma unroll
-    for (int j = 0; j < kN; ++j) p_res[j] += pp[2 * kN + i * kN + j];
-    ss += pp[kC];
-    dhp += pp[kC + 1 + i];
+    for (int u = 0; u < kChunk; ++u) {
+      const int s = s0 + u < nslices ? s0 + u : 0;
+      const float* pp = part + ((int64_t)s * T + tc) * kPartStride;
+      va[u] = *reinterpret_cast<const float4*>(pp + 2 * kN + i * kN);  // res row i
+      vc[u] = pp[i];
+      vd[u] = pp[kN + i];
+      ve[u] = pp[kC];
+      vb[u].x = pp[kC + 1 + i];
+    }
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      if (s0 + u < nslices) {
+        p_pre += vc[u];
+        p_post += vd[u];
+        p_res[0] += va[u].x;
+        p_res[1] += va[u].y;
+        p_res[2] += va[u].z;
+        p_res[3] += va[u].w;
+        ss += ve[u];
+        dhp += vb[u].x;
+      }
+    }
   }
-  const float rstd = 1.0f / sqrtf(ss / (float)K + eps);
+  // same arithmetic as the forward kernels (hardware reciprocal and
+  // reciprocal square root): this pass is one wave per four CUs, so its time
+  // is the latency of these chains
+  const float rstd = __builtin_amdgcn_rsqf(ss / (float)K + eps);
   const float q_pre = rstd * p_pre, q_post = rstd * p_post;
   const float l_pre = a_pre * q_pre + bias[i];
   const float l_post = a_post * q_post + bias[kN + i];
-  const float s_pre = sigmoid(l_pre), s_post = sigmoid(l_post);
+  const float s_pre = __builtin_amdgcn_rcpf(1.0f + expf(-l_pre));
+  const float s_post = __builtin_amdgcn_rcpf(1.0f + expf(-l_post));
   float q_res[kN], m0[kN], mx = -__builtin_huge_valf();
 #pragma unroll
   for (int j = 0; j < kN; ++j) {
@@ -283,11 +309,11 @@ __global__ __launch_bounds__(kCoefThreads) void bwd_coef_kernel(
     float r = 0.f;
 #pragma unroll
     for (int j = 0; j < kN; ++j) r += m0[j] * v[j];
-    u = 1.0f / r;  // row i now sums to 1
+    u = __builtin_amdgcn_rcpf(r);  // row i now sums to 1
 #pragma unroll
     for (int j = 0; j < kN; ++j) {
       const float cj = quad_sum(u * m0[j] * v[j]);  // column j sum
-      v[j] = v[j] / cj;
+      v[j] = v[j] * __builtin_amdgcn_rcpf(cj);
     }
     h[(it * 2 + 0) * 64] = u;
     h[(it * 2 + 1) * 64] = v[i];
@@ -317,13 +343,13 @@ __global__ __launch_bounds__(kCoefThreads) void bwd_coef_kernel(
     for (int j = 0; j < kN; ++j) {
       const float y = m0[j] * u_s * v_s[j];
       const float colacc = quad_sum(G[j] * y);
-      G[j] = (G[j] - colacc) * (v_s[j] / v_p[j]);
+      G[j] = (G[j] - colacc) * (v_s[j] * __builtin_amdgcn_rcpf(v_p[j]));
     }
     // row step: X = M0·u_p·v_p, Y = M0·u_s·v_p, divisor r = u_p/u_s
     float rowacc = 0.f;
 #pragma unroll
     for (int j = 0; j < kN; ++j) rowacc += G[j] * (m0[j] * u_s * v_p[j]);
-    const float rinv = u_s / u_p;
+    const float rinv = u_s * __builtin_amdgcn_rcpf(u_p);
 #pragma unroll
     for (int j = 0; j < kN; ++j) G[j] = (G[j] - rowacc) * rinv;
   }
@@ -609,13 +635,70 @@ __global__ __launch_bounds__(kDxThreads, 2) void bwd_dx_kernel(
   }
 }
 
-// dφ = Σ_s part[s] in split order
-__global__ __launch_bounds__(256) void dphi_sum_kernel(const float* __restrict__ part,
-                                                       float* __restrict__ dphi, int64_t KC, int S) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+// dφ = Σ_s part[s] in split order.  Workgroup 0 sums the dbias / dα rows
+// instead (one row per 16 tokens), in a fixed order.
+__global__ __launch_bounds__(256) void dphi_bias_sum_kernel(const float* __restrict__ part,
+                                                            float* __restrict__ dphi, int64_t KC, int S,
+                                                            const float* __restrict__ dlog,
+                                                            const float* __restrict__ dal,
+                                                            float* __restrict__ dbias,
+                                                            float* __restrict__ dalpha, int64_t R) {
+  if (blockIdx.x == 0) {
+    // thread t adds rows t, t + 256, … (all of a row's loads in flight at
+    // once); the per-thread sums then meet in LDS: eight partial sums of 32
+    // threads per column, then the eight in index order
+    constexpr int kV = kC + 3;
+    __shared__ float red[kV][256 + 1];
+    __shared__ float red2[kV][8];
+    const int t = threadIdx.x;
+    float acc[kV];
+#pragma unroll
+    for (int c = 0; c < kV; ++c) acc[c] = 0.f;
+    for (int64_t r = t; r < R; r += 256) {
+      float4 v[kC / 4 + 1];
+#pragma unroll
+      for (int q = 0; q < kC / 4; ++q) v[q] = reinterpret_cast<const float4*>(dlog + r * kC)[q];
+      v[kC / 4] = reinterpret_cast<const float4*>(dal + r * 4)[0];
+#pragma unroll
+      for (int q = 0; q < kC / 4 + 1; ++q) {
+        const float w[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * q + e < kV) acc[4 * q + e] += w[e];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kV; ++c) red[c][t] = acc[c];
+    __syncthreads();
+    if (t < kV * 8) {
+      const int c = t >> 3, part = t & 7;
+      float v = 0.f;
+      for (int k = 0; k < 32; ++k) v += red[c][part * 32 + k];
+      red2[c][part] = v;
+    }
+    __syncthreads();
+    if (t < kV) {
+      float v = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v += red2[t][k];
+      if (t < kC) dbias[t] = v;
+      else if (dalpha) dalpha[t - kC] = v;
+    }
+    return;
+  }
+  const int64_t i = (int64_t)(blockIdx.x - 1) * 256 + threadIdx.x;
   if (i >= KC) return;
+  // the splits' loads in flight together, summed in split order
+  constexpr int kChunk = 8;
   float s = 0.f;
-  for (int j = 0; j < S; ++j) s += part[(int64_t)j * KC + i];
+  for (int j0 = 0; j0 < S; j0 += kChunk) {
+    float v[kChunk];
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) v[u] = part[(int64_t)(j0 + u < S ? j0 + u : 0) * KC + i];
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u)
+      if (j0 + u < S) s += v[u];
+  }
   dphi[i] = s;
 }
 
@@ -667,7 +750,7 @@ size_t pre_bwd_mfma_workspace_bytes(const mhc_desc& d) { return bwdm::layout(d).
 
 hipError_t launch_pre_bwd_mfma(const mhc_desc& d, const void* dh, const void* x, const float* phi,
                                const float* bias, const float* dH_post, const float* dH_res,
-                               void* dx, float* dphi, void* ws, float** dlog_out, float** dal_out,
+                               void* dx, float* dphi, float* dbias, float* dalpha, void* ws,
                                hipStream_t s) {
   using namespace bwdm;
   const Layout L = layout(d);
@@ -677,8 +760,6 @@ hipError_t launch_pre_bwd_mfma(const mhc_desc& d, const void* dh, const void* x,
   float* dlog = reinterpret_cast<float*>(w + L.dlog);
   float* dal = reinterpret_cast<float*>(w + L.dal);
   float* dphi_part = reinterpret_cast<float*>(w + L.dphi);
-  *dlog_out = dlog;  // one row per 16 tokens
-  *dal_out = dal;
   const int64_t T = d.T;
   const int K = kN * d.D;
   const dim3 pgrid((unsigned)L.S, (unsigned)L.PS);
@@ -701,8 +782,8 @@ hipError_t launch_pre_bwd_mfma(const mhc_desc& d, const void* dh, const void* x,
                      static_cast<uint16_t*>(dx), dphi_part, T, d.D, tps);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t KC = (int64_t)K * kC;
-  hipLaunchKernelGGL(dphi_sum_kernel, dim3((unsigned)((KC + 255) / 256)), dim3(256), 0, s, dphi_part,
-                     dphi, KC, L.TS);
+  hipLaunchKernelGGL(dphi_bias_sum_kernel, dim3((unsigned)((KC + 255) / 256 + 1)), dim3(256), 0, s,
+                     dphi_part, dphi, KC, L.TS, dlog, dal, dbias, dalpha, (int64_t)((T + 15) / 16));
   return hipGetLastError();
 }
 

@@ -41,7 +41,7 @@ bool pre_bwd_mfma_eligible(const mhc_desc& d);
 size_t pre_bwd_mfma_workspace_bytes(const mhc_desc& d);
 hipError_t launch_pre_bwd_mfma(const mhc_desc& d, const void* dh, const void* x, const float* phi,
                                const float* bias, const float* dH_post, const float* dH_res,
-                               void* dx, float* dphi, void* ws, float** dlog, float** dal,
+                               void* dx, float* dphi, float* dbias, float* dalpha, void* ws,
                                hipStream_t s);
 hipError_t launch_pre_bwd(const mhc_desc& d, const void* dh, const void* x, const float* phi,
                           const float* bias, const float* dH_post, const float* dH_res, void* dx,
