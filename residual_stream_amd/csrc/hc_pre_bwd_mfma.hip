@@ -106,6 +106,17 @@ __global__ __launch_bounds__(64 * W, 1) void bwd_proj_kernel(
     hs[SL] = ld16(rh, (uint32_t)((row * D + d0 + 8 * g) * 2));
   };
 
+  // The first three blocks' loads go out first, so that x and dh stream while
+  // φ is staged (vector memory completes in order: the φ loads below arrive
+  // after them, and the block loop is entered with nothing outstanding).
+  // (kept in issue order: the wait counts in the loop assume slot 0 oldest)
+  load_blk(0, std::integral_constant<int, 0>{});
+  __builtin_amdgcn_sched_barrier(0);
+  load_blk(1, std::integral_constant<int, 1>{});
+  __builtin_amdgcn_sched_barrier(0);
+  load_blk(2, std::integral_constant<int, 2>{});
+  __builtin_amdgcn_sched_barrier(0);
+
   // φ: stream by stream through LDS (the red buffer), all global loads of a
   // thread issued before the first LDS write
   uint4 bfr[kN][2];
@@ -143,16 +154,6 @@ __global__ __launch_bounds__(64 * W, 1) void bwd_proj_kernel(
       __syncthreads();
     }
   }
-
-  // the first blocks go out after φ, so that the wait counts at the top of
-  // the block loop are the same on entry and on every later pass
-  // (kept in issue order: the wait counts in the loop assume slot 0 oldest)
-  load_blk(0, std::integral_constant<int, 0>{});
-  __builtin_amdgcn_sched_barrier(0);
-  load_blk(1, std::integral_constant<int, 1>{});
-  __builtin_amdgcn_sched_barrier(0);
-  load_blk(2, std::integral_constant<int, 2>{});
-  __builtin_amdgcn_sched_barrier(0);
 
   auto block = [&](int b, auto slot_c) {
     constexpr int SL = decltype(slot_c)::value;
