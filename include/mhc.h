@@ -91,7 +91,10 @@ size_t mhc_pre_workspace_bytes(const mhc_desc* desc);
  * bf16, N = 4, D = 5120 or 2560 the call splits each token's reduction across
  * workgroups that exchange partial sums through the workspace, tagged per
  * call, so two calls that share a workspace must not overlap in time (on one
- * stream they never do). */
+ * stream they never do).  Those workgroups wait for each other with bounded
+ * waits; should one never arrive (e.g. far too few free compute units), the
+ * affected tokens get NaN in h and in the coefficients rather than a hang or
+ * silently wrong values. */
 mhc_status mhc_pre(const mhc_desc* desc, const void* x, const float* phi, const float* bias,
                    void* h, float* H_pre, float* H_post, float* H_res,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);

@@ -33,9 +33,10 @@
 // consecutive tickets (modulo the grid size).  So at any time at most two
 // groups (the newest, and the one the modulo wraps) have members not yet
 // running; every other group has all its members running and finishes
-// without help, freeing CUs for the missing members.  Each wait is also bounded (a wait
-// that exceeds its bound gives up: that call's results are then wrong, never a
-// hang).
+// without help, freeing CUs for the missing members.  Each wait is also
+// bounded: a wait that runs out gives up and writes NaN coefficients (and so
+// NaN h) for the tokens of that tile — never a hang, never silently wrong
+// values.
 #include "mhc_coef.h"
 #include "mhc_internal.h"
 
@@ -394,10 +395,14 @@ __global__ __launch_bounds__(kThreads, 1) void hc_pre_coop_kernel(
             __builtin_amdgcn_s_sleep(2);
             load_all(p - kTake);
           }
+          // a wait that ran out (a group member never published) poisons the
+          // tile's coefficients, and so h, H_pre, H_post and H_res of its
+          // tokens, with NaN: a loud failure instead of silently wrong values
+          const float poison = spins < kSpinLimit ? 0.f : __builtin_nanf("");
           const int bt = (p - kTake) & 1;
           const int ring = (int)((p - kTake) % (2 * kBatch)) * kShare;  // ring row of the tile's share
           // (a): slice sums in a fixed order; quad sum of the squares
-          float pre = 0.f, ss = 0.f;
+          float pre = poison, ss = poison;
 #pragma unroll
           for (int i = 0; i < S; ++i) pre += value_of(va[i]);
 #pragma unroll
@@ -414,7 +419,7 @@ __global__ __launch_bounds__(kThreads, 1) void hc_pre_coop_kernel(
             r[kRest + 1 + n] = hp;
           }
           // (b): slice sums of the share's post + res logits
-          float v = 0.f;
+          float v = poison;
 #pragma unroll
           for (int i = 0; i < SB; ++i) v += value_of(vb[i]);
           if (kShare == 1) v += __shfl_xor(v, 32, kWave);
