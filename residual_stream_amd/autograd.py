@@ -1,0 +1,133 @@
+"""torch.autograd integration of the mHC operator pair, with the recompute policy.
+
+One residual block of a model that uses mHC (openPangu 2.0 analysis, §5.3 "mHC"
+formula block) reads the N-stream state x through hc_pre, runs its sublayer F on
+h, and writes back through hc_post:
+
+    h, H_pre, H_post, H_res = hc_pre(x; φ, b, α)
+    y = F(h)
+    x_next = H_res · x + H_post ⊗ y
+
+`MHCBlock` wraps that with the four C-ABI calls as autograd functions.  What the
+backward keeps follows the intra-layer recompute paragraph of the Ascend mHC
+Triton article: only the hc_pre input x and the sublayer output y (plus the
+80 bytes per token of H_post / H_res); `mhc_pre_bwd` recomputes the norm, the
+logits and the Sinkhorn rounds from x.  With ``recompute=True`` the sublayer is
+checkpointed too, so not even h or the sublayer's own activations are kept.
+
+The two backward calls share one dx buffer, as the C ABI intends: the hc_post
+backward writes its part of dx, and the hc_pre backward adds its own to it in
+place.  The hc_post node therefore hands its dx to the hc_pre node of the same
+block instead of returning it; the hc_pre node returns the total.
+
+Every step runs in the library's kernels; this module only wires them into
+autograd.  It needs a GPU and the built library, like the binding.
+"""
+
+from __future__ import annotations
+
+import torch
+from torch.utils.checkpoint import checkpoint
+
+from . import mhc
+
+
+class _DxHandoff:
+    """Carries hc_post's dx to the hc_pre backward of the same block."""
+
+    __slots__ = ("dx",)
+
+    def __init__(self):
+        self.dx = None
+
+
+class _Pre(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, phi, bias, alpha, iters, eps, handoff):
+        alphas = tuple(float(a) for a in alpha.tolist())  # alpha lives on the host
+        h, Hp, Hq, Hr = mhc.mhc_pre(x, phi, bias, iters=iters, eps=eps, alphas=alphas)
+        ctx.save_for_backward(x, phi, bias)
+        ctx.cfg = (iters, eps, alphas, alpha.requires_grad)
+        ctx.handoff = handoff
+        ctx.mark_non_differentiable(Hp)  # used only inside the collapse
+        return h, Hp, Hq, Hr
+
+    @staticmethod
+    def backward(ctx, dh, _dHp, dHq, dHr):
+        x, phi, bias = ctx.saved_tensors
+        iters, eps, alphas, want_dalpha = ctx.cfg
+        T, N, D = x.shape
+        dx = ctx.handoff.dx
+        ctx.handoff.dx = None
+        if dx is None:  # hc_post's output took no gradient
+            dx = torch.zeros_like(x)
+        if dh is None:
+            dh = torch.zeros((T, D), dtype=x.dtype, device=x.device)
+        if dHq is None:
+            dHq = torch.zeros((T, N), dtype=torch.float32, device=x.device)
+        if dHr is None:
+            dHr = torch.zeros((T, N, N), dtype=torch.float32, device=x.device)
+        dx, dphi, dbias, dalpha = mhc.mhc_pre_bwd(
+            dh.contiguous(), x, phi, bias, dHq.contiguous(), dHr.contiguous(), dx,
+            iters=iters, eps=eps, alphas=alphas, want_dalpha=want_dalpha)
+        dalpha = dalpha.cpu() if want_dalpha else None
+        return dx, dphi, dbias, dalpha, None, None, None
+
+
+class _Post(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, y, H_post, H_res, handoff):
+        x_next = mhc.mhc_post(x, y, H_post, H_res)
+        ctx.save_for_backward(x, y, H_post, H_res)
+        ctx.handoff = handoff
+        return x_next
+
+    @staticmethod
+    def backward(ctx, dx_next):
+        x, y, H_post, H_res = ctx.saved_tensors
+        dx, dy, dHq, dHr = mhc.mhc_post_bwd(dx_next.contiguous(), x, y, H_post, H_res)
+        ctx.handoff.dx = dx  # the hc_pre backward of this block adds to it
+        return None, dy, dHq, dHr, None
+
+
+class MHCBlock(torch.nn.Module):
+    """One mHC residual block around `sublayer` (a module mapping h[T, D] to
+    y[T, D] in the I/O dtype).
+
+    Parameters: φ[N·D, N²+2N] and b[N²+2N] (fp32, on the GPU) and the three gate
+    scalars α = (α_pre, α_post, α_res) as a host tensor (their values are
+    launch parameters; their gradient comes back from the GPU).  x is
+    [T, N, D] or [B, S, N, D], fp32 or bf16, on the GPU.
+    """
+
+    def __init__(self, sublayer: torch.nn.Module, n_streams: int, hidden: int, *,
+                 iters: int = 20, eps: float = 1e-6, alpha=(0.01, 0.01, 0.01),
+                 train_alpha: bool = False, recompute: bool = False, device="cuda"):
+        super().__init__()
+        N, D = n_streams, hidden
+        C = N * N + 2 * N
+        self.sublayer = sublayer
+        self.N, self.D, self.iters, self.eps, self.recompute = N, D, iters, eps, recompute
+        self.phi = torch.nn.Parameter(torch.randn(N * D, C, device=device) / (N * D) ** 0.5)
+        self.bias = torch.nn.Parameter(torch.zeros(C, device=device))
+        self.alpha = torch.nn.Parameter(torch.tensor(alpha, dtype=torch.float32),
+                                        requires_grad=train_alpha)
+
+    def _pre_sub(self, x, handoff):
+        h, _Hp, Hq, Hr = _Pre.apply(x, self.phi, self.bias, self.alpha, self.iters, self.eps, handoff)
+        return self.sublayer(h), Hq, Hr
+
+    def forward(self, x):
+        shape = x.shape
+        if x.dim() == 4:
+            x = x.reshape(-1, shape[-2], shape[-1])
+        if x.shape[1:] != (self.N, self.D):
+            raise ValueError(f"expected [..., {self.N}, {self.D}] state, got {tuple(shape)}")
+        x = x.contiguous()
+        handoff = _DxHandoff()
+        if self.recompute and torch.is_grad_enabled():
+            y, Hq, Hr = checkpoint(self._pre_sub, x, handoff, use_reentrant=False)
+        else:
+            y, Hq, Hr = self._pre_sub(x, handoff)
+        x_next = _Post.apply(x, y.contiguous(), Hq, Hr, handoff)
+        return x_next.reshape(shape)

@@ -1,0 +1,105 @@
+"""MHCBlock (torch.autograd wiring of the four C-ABI calls) against the fp64
+oracle: x_next, and the gradients of a linear loss with respect to x, φ, b and
+α, through a sublayer y = F(h).  The sublayer runs in torch on the GPU; the
+oracle reference is fed the very h, y and dh values the GPU path produced at
+the sublayer boundary (the sublayer is not part of mHC), so the comparison is
+of the mHC steps alone, to the kernels' tolerance."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import mhc_oracle as O
+from residual_stream_amd.inputs import make_inputs
+
+from mhc_testlib import TOL, assert_close, dev, host, tdtype
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class _Scale(torch.nn.Module):
+    """y = h ⊙ c with a fixed per-d vector c (a stand-in sublayer with an exact backward)."""
+
+    def __init__(self, c):
+        super().__init__()
+        self.register_buffer("c", c)
+
+    def forward(self, h):
+        return h * self.c
+
+
+def _run(inp, recompute, seed=7):
+    from residual_stream_amd.autograd import MHCBlock
+
+    io = inp.io
+    rng = np.random.default_rng(seed)
+    c = dev(rng.uniform(0.5, 1.5, inp.D).astype(np.float32), io)
+    g = dev(rng.standard_normal((inp.T, inp.N, inp.D)).astype(np.float32), io)
+    block = MHCBlock(_Scale(c), inp.N, inp.D, iters=inp.iters, eps=inp.eps, alpha=inp.alphas,
+                     train_alpha=True, recompute=recompute)
+    with torch.no_grad():
+        block.phi.copy_(dev(inp.phi))
+        block.bias.copy_(dev(inp.bias))
+    x = dev(inp.x, io).requires_grad_(True)
+    # capture the sublayer boundary values for the oracle
+    seen = {}
+    block.sublayer.register_forward_hook(lambda m, a, out: seen.update(h=a[0].detach(), y=out.detach()))
+    xn = block(x)
+    (xn.float() * g.float()).sum().backward()
+    torch.cuda.synchronize()
+    return block, x, xn, g, c, seen
+
+
+@pytest.mark.parametrize("io,T,D", [("bf16", 70, 256), ("f32", 33, 64), ("bf16", 5, 512)])
+def test_block_matches_oracle(io, T, D):
+    _say(f"[autograd] io={io} T={T} D={D}")
+    inp = make_inputs(T, 4, D, io=io, seed=11, alpha=0.3)
+    block, x, xn, g, c, seen = _run(inp, recompute=False)
+    h_gpu, y_gpu = host(seen["h"]), host(seen["y"])
+    ref = O.hc_pre(inp.x, inp.phi, inp.bias, inp.alphas, inp.eps, inp.iters)
+    tol = TOL[io]
+    assert_close("h", h_gpu, ref["h"], tol)
+    assert_close("x_next", host(xn), O.hc_post(inp.x, y_gpu, ref["H_post"], ref["H_res"]), tol)
+    # backward reference: the same dxn; dy through the oracle; dh = dy ⊙ c rounded as torch does
+    gn = host(g)
+    dx_post, dy, dHq, dHr = O.hc_post_bwd(gn, inp.x, y_gpu, ref["H_post"], ref["H_res"])
+    dy_io = torch.from_numpy(dy.astype(np.float32)).to(tdtype(io)).cuda()
+    dh = host(dy_io * c)
+    pre = O.hc_pre_bwd(dh, inp.x, inp.phi, inp.bias, dHq, dHr, inp.alphas, inp.eps, inp.iters)
+    assert_close("dx", host(x.grad), dx_post + pre["dx"], tol)
+    assert_close("dphi", host(block.phi.grad), pre["dphi"], tol)
+    assert_close("dbias", host(block.bias.grad), pre["dbias"], tol)
+    assert_close("dalpha", block.alpha.grad.double().numpy(), pre["dalpha"], tol)
+
+
+def test_recompute_gives_identical_gradients():
+    _say("[autograd] recompute on/off, bf16 T=70 D=256")
+    inp = make_inputs(70, 4, 256, io="bf16", seed=5, alpha=0.3)
+    a = _run(inp, recompute=False)
+    b = _run(inp, recompute=True)
+    assert torch.equal(a[2], b[2])
+    assert torch.equal(a[1].grad, b[1].grad)
+    assert torch.equal(a[0].phi.grad, b[0].phi.grad)
+    assert torch.equal(a[0].bias.grad, b[0].bias.grad)
+    assert torch.equal(a[0].alpha.grad, b[0].alpha.grad)
+
+
+def test_batched_state_shape():
+    _say("[autograd] [B, S, N, D] input")
+    inp = make_inputs(12, 4, 64, io="f32", seed=2)
+    from residual_stream_amd.autograd import MHCBlock
+
+    block = MHCBlock(torch.nn.Identity(), 4, 64)
+    x = dev(inp.x, "f32").reshape(3, 4, 4, 64)
+    out = block(x)
+    assert out.shape == x.shape
+    flat = block(x.reshape(12, 4, 64))
+    assert torch.equal(out.reshape(12, 4, 64), flat)
