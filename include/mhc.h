@@ -131,6 +131,25 @@ mhc_status mhc_pre_bwd(const mhc_desc* desc, const void* dh, const void* x, cons
 /* Static, NUL-terminated description of a status code. */
 const char* mhc_status_string(mhc_status status);
 
+/* Bytes of device workspace mhc_post_pre needs (the same as mhc_pre's for
+ * the same descriptor). */
+size_t mhc_post_pre_workspace_bytes(const mhc_desc* desc);
+
+/* hc_post of one layer fused with hc_pre of the next layer (openPangu 2.0
+ * analysis §11.3: the write-back, the next RMSNorm and H_pre in one pass).
+ * Computes x_next = H_res_in·x + H_post_in ⊗ y ([T][N][D], I/O dtype; the
+ * mhc_post contract) and then, on x_next as stored, hc_pre of the next layer
+ * with its phi, bias and the descriptor's Sinkhorn rounds, eps and gate
+ * scalars: h, H_pre, H_post, H_res (the mhc_pre contract).  The results equal
+ * mhc_post followed by mhc_pre bit for bit; for bf16, N = 4, D = 5120 or 2560
+ * x_next is not read back (one pass over x and y instead of a write and a
+ * re-read of x_next).  Outputs must not alias inputs; the workspace rules of
+ * mhc_pre apply. */
+mhc_status mhc_post_pre(const mhc_desc* desc, const void* x, const void* y, const float* H_post_in,
+                        const float* H_res_in, const float* phi, const float* bias, void* x_next,
+                        void* h, float* H_pre, float* H_post, float* H_res, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
 /* MHC_ABI_VERSION of the built library. */
 int mhc_abi_version(void);
 

@@ -57,8 +57,7 @@ constexpr int kW = 10;                  // compute waves, one 32-d block each
 constexpr int kThreads = (kW + 2) * 64; // + two communication waves
 constexpr int kSliceD = kW * 32;        // 320 d per slice
 constexpr int kLag = 5;                 // periods from projection to collapse
-constexpr int kAhead = 2;               // tiles whose loads are in flight
-constexpr int kSlots = kLag + kAhead;   // register buffers of x
+constexpr int kHq = kN + kN * kN;       // incoming H_post[4] and H_res[16] of a token (fused)
 constexpr int kHead = 5;                // record entries every slice needs: pre[4], ss
 constexpr int kRest = 20;               // record entries of the finishing slice: post[4], res[16]
 constexpr int kRecA = kHead * kTM;      // part A of a (tile, slice) block: [entry][token]
@@ -136,9 +135,21 @@ __device__ __forceinline__ int word_of(int c, int tk) {
 // uint64: part A [entry][token] holds pre[4] and ss (read by every slice,
 // 128 contiguous bytes per entry), part B [token][entry] post[4] and res[16]
 // (read by the slice that finishes the token).
-template <int S>
-__global__ __launch_bounds__(kThreads, 1) void hc_pre_coop_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ bias, uint16_t* __restrict__ h,
+// Calls f(integral_constant<J>) for J = 0 .. n−1 (one turn of a register ring).
+template <typename F, int... J>
+__device__ __forceinline__ void each_slot(F&& f, std::integer_sequence<int, J...>) {
+  (f(std::integral_constant<int, J>{}), ...);
+}
+
+// FUSED: x is the previous layer's state; each tile's state is first mixed
+// and written back, x_next = H_res·x + H_post ⊗ y (hc_post, in the same
+// arithmetic order as the hc_post kernel), and hc_pre then runs on x_next
+// (openPangu 2.0 analysis §11.3: merge, RMSNorm and H_pre in one pass).
+template <int S, bool FUSED>
+__device__ __forceinline__ void coop_body(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ y, const float* __restrict__ Hq_in,
+    const float* __restrict__ Hr_in, uint16_t* __restrict__ xn,
+    const float* __restrict__ bias, uint16_t* __restrict__ h,
     float* __restrict__ H_pre, float* __restrict__ H_post, float* __restrict__ H_res,
     const float* __restrict__ phi, uint64_t* ctr, uint64_t* rec, int64_t T, int Q, uint32_t tag,
     int iters, float eps, float a_pre, float a_post, float a_res) {
@@ -146,6 +157,8 @@ __global__ __launch_bounds__(kThreads, 1) void hc_pre_coop_kernel(
   constexpr int K = kN * D;
   constexpr int kShare = kTM / S;  // tokens whose gates and Sinkhorn this workgroup finishes
   static_assert(kTM % S == 0 && (S == 16 || S == 8), "slice count");
+  // periods per turn of the compute waves' register ring
+  constexpr int kTurn = FUSED ? kLag : kLag + 2;
   __shared__ __align__(16) float red[2][kW][kRecWords];  // per-wave partials in record order, by period parity
   __shared__ __align__(16) float hpre_s[2][kTM][kN];
   __shared__ float rstd_s[2][kTM];
@@ -157,6 +170,7 @@ __global__ __launch_bounds__(kThreads, 1) void hc_pre_coop_kernel(
   __shared__ float bias_s[kC];
   __shared__ __align__(16) uint4 phis[kW][kN][2][64];  // φ B fragments of each compute wave
   __shared__ int ticket_s;
+  __shared__ __align__(16) float hq_s[FUSED ? 2 : 1][kTM][kHq];  // incoming coefficients, by tile parity
 
   // Every call draws exactly gridDim.x tickets, so any run of gridDim.x
   // consecutive counter values covers each residue once: the counter needs
@@ -179,7 +193,7 @@ __global__ __launch_bounds__(kThreads, 1) void hc_pre_coop_kernel(
   // periods: a whole number of turns of the compute waves' register ring
   // (periods past the last collapse do nothing), so that their loop has a
   // single exit and keeps each slot in the same registers on every pass
-  const int64_t nper = (nloc + kLag + kSlots - 1) / kSlots * kSlots;
+  const int64_t nper = (nloc + kLag + kTurn - 1) / kTurn * kTurn;
   auto tile_of = [&](int64_t p) { return grp + p * Q; };
   auto rows_of = [&](int64_t p) -> int64_t {  // valid tokens of the group's p-th tile
     if (p < 0 || p >= nloc) return 0;
@@ -229,7 +243,10 @@ __global__ __launch_bounds__(kThreads, 1) void hc_pre_coop_kernel(
   };
 
   if (wave < kW) {
+   if constexpr (!FUSED) {
     // ================= compute waves =================
+  constexpr int kAhead = 2;              // tiles whose loads are in flight
+  constexpr int kSlots = kLag + kAhead;  // register buffers of x
   // Compute-wave lane roles: (row, g) holds token row, d block d0 + 8g .. +8.
   const int row = lane & 15, g = lane >> 4;
   const int d0 = slice * kSliceD + wave * 32;
@@ -330,6 +347,172 @@ __global__ __launch_bounds__(kThreads, 1) void hc_pre_coop_kernel(
       period(p + 5, std::integral_constant<int, 5>{});
       period(p + 6, std::integral_constant<int, 6>{});
     }
+   } else {
+    // ============ compute waves, fused with the previous hc_post ============
+  // Ring of kLag registers sets holding x_next of the tiles waiting for their
+  // H_pre (indexed by p mod kLag); one set for the next tile's incoming state
+  // and y.  In period p: collapse tile p − kLag (freeing its set), mix tile p
+  // into that set (x_next = H_res·x + H_post ⊗ y, written back), issue the
+  // loads of tile p + 1 into the incoming set, project tile p.
+  const int row = lane & 15, g = lane >> 4;
+  const int d0 = slice * kSliceD + wave * 32;
+  uint4 xs[kLag][kN];
+  uint4 raw[kN], yr;
+  float4 hq_reg;  // incoming coefficients of the next tile (waves 0, 1; zero elsewhere)
+  auto load_raw = [&](int64_t p) {
+    const int64_t rows = rows_of(p);
+    const int64_t t0 = rows > 0 ? tile_of(p) * kTM : 0;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(x + t0 * K, (uint32_t)(rows * K * 2));
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(y + t0 * D, (uint32_t)(rows * D * 2));
+#pragma unroll
+    for (int n = 0; n < kN; ++n) raw[n] = ld16(rs, (uint32_t)(((row * kN + n) * D + d0 + 8 * g) * 2));
+    yr = ld16(ry, (uint32_t)((row * D + d0 + 8 * g) * 2));
+  };
+  // lanes i < 80 of waves 0, 1 load float4 i of a tile's incoming
+  // coefficients (token i/5: H_res row-major in chunks 0..3, H_post in 4).
+  // Every wave issues the load (others through an empty descriptor) so that
+  // all waves see the same vector-memory queue and the same wait counts.
+  const int ci = wave * 64 + lane, ct = ci / 5, cc = ci % 5;
+  const bool c_lane = ci < kTM * 5;
+  auto load_coef = [&](int64_t p) {
+    const int64_t rows = wave < 2 ? rows_of(p) : 0;
+    const int64_t t0 = rows > 0 ? tile_of(p) * kTM : 0;
+    const bool in = c_lane && ct < rows;
+    constexpr uint32_t kOut = 0x7FFFFFF0u;  // past every descriptor: reads zero
+    // both descriptors are wave-uniform; each lane reads one of them and
+    // zero from the other
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(Hr_in + t0 * kN * kN, (uint32_t)(rows * kN * kN * 4));
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Hq_in + t0 * kN, (uint32_t)(rows * kN * 4));
+    const uint4 vr = ld16(rr, in && cc < 4 ? (uint32_t)((ct * kN * kN + 4 * cc) * 4) : kOut);
+    const uint4 vq = ld16(rq, in && cc == 4 ? (uint32_t)(ct * kN * 4) : kOut);
+    hq_reg = make_float4(__uint_as_float(vr.x | vq.x), __uint_as_float(vr.y | vq.y),
+                         __uint_as_float(vr.z | vq.z), __uint_as_float(vr.w | vq.w));
+  };
+  auto stage_coef = [&](int64_t p) {  // hq_reg → hq_s[p & 1]
+    if (wave < 2 && c_lane) *reinterpret_cast<float4*>(&hq_s[p & 1][ct][cc < 4 ? kN + 4 * cc : 0]) = hq_reg;
+  };
+  stage_phi([&]() {
+    load_coef(0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_raw(0);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_coef(0);
+  });
+  // the sets of tiles before the first are collapsed into dropped stores
+#pragma unroll
+  for (int s = 0; s < kLag; ++s)
+#pragma unroll
+    for (int n = 0; n < kN; ++n) xs[s][n] = make_uint4(0u, 0u, 0u, 0u);
+  const uint4(*bf)[2][64] = phis[wave];
+
+    auto period = [&](int64_t p_in, auto j_c) {
+      constexpr int J = decltype(j_c)::value;  // p mod kLag: set of tile p − kLag, then of tile p
+      // p passes through an SGPR the compiler cannot see into, so that the
+      // addresses of the unrolled periods are computed where used rather than
+      // all held from the loop head (scalar registers are short here)
+      int p32 = (int)p_in;
+      asm volatile("" : "+s"(p32));
+      const int64_t p = p32;
+      // collapse tile p − kLag
+      {
+        const int64_t rows = rows_of(p - kLag);
+        uint16_t* base = h + (rows > 0 ? tile_of(p - kLag) * kTM * D : 0);
+        const __amdgpu_buffer_rsrc_t hr = make_rsrc(base, (uint32_t)(rows * D * 2));
+        const float4 hw = *reinterpret_cast<const float4*>(&hpre_s[(p - kLag) & 1][row][0]);
+        const float hv[kN] = {hw.x, hw.y, hw.z, hw.w};
+        float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int n = 0; n < kN; ++n) {
+          uint4 a = xs[J][n];
+          opaque(a);
+          o[0] += hv[n] * bf16_lo(a.x);
+          o[1] += hv[n] * bf16_hi(a.x);
+          o[2] += hv[n] * bf16_lo(a.y);
+          o[3] += hv[n] * bf16_hi(a.y);
+          o[4] += hv[n] * bf16_lo(a.z);
+          o[5] += hv[n] * bf16_hi(a.z);
+          o[6] += hv[n] * bf16_lo(a.w);
+          o[7] += hv[n] * bf16_hi(a.w);
+        }
+        st16(hr, (uint32_t)((row * D + d0 + 8 * g) * 2),
+             make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                        pack_bf16x2(o[6], o[7])));
+      }
+      // coefficients of tile p + 1, ahead of its state loads
+      load_coef(p + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      // x_next of tile p: H_res·x + H_post ⊗ y in the hc_post kernel's order
+      // (fused multiply-adds over m after H_post·y), rounded to bf16, written
+      // back and kept as the state hc_pre reads
+      {
+        const int64_t rows = rows_of(p);
+        const int64_t t0 = rows > 0 ? tile_of(p) * kTM : 0;
+        const __amdgpu_buffer_rsrc_t ro = make_rsrc(xn + t0 * K, (uint32_t)(rows * K * 2));
+        const float* hq = hq_s[p & 1][row];
+#pragma unroll
+        for (int n = 0; n < kN; ++n) {
+          __builtin_amdgcn_sched_barrier(0);
+          const float4 r4 = *reinterpret_cast<const float4*>(hq + kN + kN * n);  // H_res row n
+          const float hr_n[kN] = {r4.x, r4.y, r4.z, r4.w};
+          const float hp_n = hq[n];
+          uint32_t w[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t yw = (&yr.x)[q];
+            float o[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              float a = hp_n * (e ? bf16_hi(yw) : bf16_lo(yw));
+#pragma unroll
+              for (int m = 0; m < kN; ++m) {
+                const uint32_t xw = (&raw[m].x)[q];
+                a = __builtin_fmaf(hr_n[m], e ? bf16_hi(xw) : bf16_lo(xw), a);
+              }
+              o[e] = a;
+            }
+            w[q] = pack_bf16x2(o[0], o[1]);
+          }
+          xs[J][n] = make_uint4(w[0], w[1], w[2], w[3]);
+          st16(ro, (uint32_t)(((row * kN + n) * D + d0 + 8 * g) * 2), xs[J][n]);
+        }
+      }
+      // loads of tile p + 1 into the incoming set just consumed
+      load_raw(p + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      // projection and sum of squares of tile p
+      {
+        f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+        float ss = 0.f;
+#pragma unroll
+        for (int n = 0; n < kN; ++n) {
+          // one stream's B fragments at a time (registers are short here)
+          __builtin_amdgcn_sched_barrier(0);
+          const uint4 a = xs[J][n];
+          acc0 = mfma(a, bf[n][0][lane], acc0);
+          acc1 = mfma(a, bf[n][1][lane], acc1);
+          ss = dot2(a.x, ss);
+          ss = dot2(a.y, ss);
+          ss = dot2(a.z, ss);
+          ss = dot2(a.w, ss);
+        }
+        float* rw = red[p & 1][wave];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          rw[word_of(row, 4 * g + q)] = acc0[q];
+          if (row < kC - 16) rw[word_of(16 + row, 4 * g + q)] = acc1[q];
+        }
+        ss += __shfl_xor(ss, 16, kWave);
+        ss += __shfl_xor(ss, 32, kWave);
+        if (g == 0) rw[kSSWord + row] = ss;
+      }
+      stage_coef(p + 1);
+      __syncthreads();
+    };
+
+    // whole turns of the register ring, no early exit
+    for (int64_t p = 0; p < nper; p += kLag)
+      each_slot([&](auto j) { period(p + decltype(j)::value, j); }, std::make_integer_sequence<int, kLag>{});
+   }
   } else {
     // ================= communication waves =================
     // Wave X = 0, 1 owns the tiles of parity X: in periods p ≡ X (mod 2) it
@@ -491,6 +674,30 @@ __global__ __launch_bounds__(kThreads, 1) void hc_pre_coop_kernel(
   }
 }
 
+#define MHC_COOP_PARAMS                                                                          \
+  const uint16_t *__restrict__ x, const uint16_t *__restrict__ y, const float *__restrict__ Hq_in, \
+      const float *__restrict__ Hr_in, uint16_t *__restrict__ xn, const float *__restrict__ bias,  \
+      uint16_t *__restrict__ h, float *__restrict__ H_pre, float *__restrict__ H_post,             \
+      float *__restrict__ H_res, const float *__restrict__ phi, uint64_t *ctr, uint64_t *rec,      \
+      int64_t T, int Q, uint32_t tag, int iters, float eps, float a_pre, float a_post, float a_res
+#define MHC_COOP_ARGS \
+  x, y, Hq_in, Hr_in, xn, bias, h, H_pre, H_post, H_res, phi, ctr, rec, T, Q, tag, iters, eps, a_pre, a_post, a_res
+
+// hc_pre (y, Hq_in, Hr_in, xn unused)
+template <int S>
+__global__ __launch_bounds__(kThreads, 1) void hc_pre_coop_kernel(MHC_COOP_PARAMS) {
+  coop_body<S, false>(MHC_COOP_ARGS);
+}
+
+// hc_post of a layer fused with hc_pre of the next
+template <int S>
+__global__ __launch_bounds__(kThreads, 1) void hc_post_pre_coop_kernel(MHC_COOP_PARAMS) {
+  coop_body<S, true>(MHC_COOP_ARGS);
+}
+
+#undef MHC_COOP_PARAMS
+#undef MHC_COOP_ARGS
+
 // Tags of the exchange records: one per call, not repeated for 2^31 calls in
 // a process; the top bit is set so that zeroed memory never matches.
 uint32_t next_tag() {
@@ -515,9 +722,12 @@ size_t pre_coop_workspace_bytes(const mhc_desc& d) {
   return coop::kHeader + align256(ntiles * S * coop::kRecWords * sizeof(uint64_t));
 }
 
-hipError_t launch_pre_coop(const mhc_desc& d, const void* x, const float* phi, const float* bias,
-                           void* h, float* H_pre, float* H_post, float* H_res, void* ws,
-                           hipStream_t s) {
+namespace {
+
+template <bool FUSED>
+hipError_t launch_coop(const mhc_desc& d, const void* x, const void* y, const float* Hq_in,
+                       const float* Hr_in, void* x_next, const float* phi, const float* bias, void* h,
+                       float* H_pre, float* H_post, float* H_res, void* ws, hipStream_t s) {
   const int S = d.D / coop::kSliceD;
   const int Q = device_cu_count() / S;
   if (Q < 1) return hipErrorInvalidConfiguration;
@@ -525,18 +735,37 @@ hipError_t launch_pre_coop(const mhc_desc& d, const void* x, const float* phi, c
   uint64_t* ctr = reinterpret_cast<uint64_t*>(w);
   uint64_t* rec = reinterpret_cast<uint64_t*>(w + coop::kHeader);
   const uint16_t* xp = static_cast<const uint16_t*>(x);
+  const uint16_t* yp = static_cast<const uint16_t*>(y);
+  uint16_t* xnp = static_cast<uint16_t*>(x_next);
   uint16_t* hp = static_cast<uint16_t*>(h);
   const uint32_t tag = coop::next_tag();
   const dim3 grid((unsigned)(Q * S)), block(coop::kThreads);
   if (S == 16)
-    hipLaunchKernelGGL((coop::hc_pre_coop_kernel<16>), grid, block, 0, s, xp, bias, hp, H_pre,
-                       H_post, H_res, phi, ctr, rec, (int64_t)d.T, Q, tag, d.sinkhorn_iters, d.eps,
-                       d.alpha_pre, d.alpha_post, d.alpha_res);
+    hipLaunchKernelGGL((FUSED ? coop::hc_post_pre_coop_kernel<16> : coop::hc_pre_coop_kernel<16>), grid, block, 0, s, xp, yp, Hq_in, Hr_in,
+                       xnp, bias, hp, H_pre, H_post, H_res, phi, ctr, rec, (int64_t)d.T, Q, tag,
+                       d.sinkhorn_iters, d.eps, d.alpha_pre, d.alpha_post, d.alpha_res);
   else
-    hipLaunchKernelGGL((coop::hc_pre_coop_kernel<8>), grid, block, 0, s, xp, bias, hp, H_pre,
-                       H_post, H_res, phi, ctr, rec, (int64_t)d.T, Q, tag, d.sinkhorn_iters, d.eps,
-                       d.alpha_pre, d.alpha_post, d.alpha_res);
+    hipLaunchKernelGGL((FUSED ? coop::hc_post_pre_coop_kernel<8> : coop::hc_pre_coop_kernel<8>), grid, block, 0, s, xp, yp, Hq_in, Hr_in,
+                       xnp, bias, hp, H_pre, H_post, H_res, phi, ctr, rec, (int64_t)d.T, Q, tag,
+                       d.sinkhorn_iters, d.eps, d.alpha_pre, d.alpha_post, d.alpha_res);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_pre_coop(const mhc_desc& d, const void* x, const float* phi, const float* bias,
+                           void* h, float* H_pre, float* H_post, float* H_res, void* ws,
+                           hipStream_t s) {
+  return launch_coop<false>(d, x, nullptr, nullptr, nullptr, nullptr, phi, bias, h, H_pre, H_post,
+                            H_res, ws, s);
+}
+
+hipError_t launch_post_pre_coop(const mhc_desc& d, const void* x, const void* y, const float* H_post_in,
+                                const float* H_res_in, void* x_next, const float* phi, const float* bias,
+                                void* h, float* H_pre, float* H_post, float* H_res, void* ws,
+                                hipStream_t s) {
+  return launch_coop<true>(d, x, y, H_post_in, H_res_in, x_next, phi, bias, h, H_pre, H_post, H_res,
+                           ws, s);
 }
 
 }  // namespace mhc

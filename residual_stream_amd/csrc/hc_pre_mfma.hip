@@ -519,4 +519,18 @@ hipError_t launch_pre(const mhc_desc& d, const void* x, const float* phi, const 
   return launch_mfma<kF32, 4, 20>(d, pc, x, phi, bias, h, H_pre, H_post, H_res, ws, s);
 }
 
+hipError_t launch_post_pre(const mhc_desc& d, const void* x, const void* y, const float* H_post_in,
+                           const float* H_res_in, void* x_next, const float* phi, const float* bias,
+                           void* h, float* H_pre, float* H_post, float* H_res, void* ws, hipStream_t s) {
+  if (pre_coop_eligible(d) && pick_pre(d).tm != 0) {
+    if (launch_post_pre_coop(d, x, y, H_post_in, H_res_in, x_next, phi, bias, h, H_pre, H_post, H_res,
+                             ws, s) == hipSuccess)
+      return hipSuccess;
+    (void)hipGetLastError();  // launch refused: clear the error and take the two kernels
+  }
+  const hipError_t e = launch_post(d, x, y, H_post_in, H_res_in, x_next, s);
+  if (e != hipSuccess) return e;
+  return launch_pre(d, x_next, phi, bias, h, H_pre, H_post, H_res, ws, s);
+}
+
 }  // namespace mhc

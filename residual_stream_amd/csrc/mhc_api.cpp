@@ -162,4 +162,33 @@ mhc_status mhc_pre_bwd(const mhc_desc* d, const void* dh, const void* x, const f
                                       dalpha, workspace, stream));
 }
 
+size_t mhc_post_pre_workspace_bytes(const mhc_desc* d) {
+  if (check_desc(d) != MHC_OK) return 0;
+  return mhc::pre_workspace_bytes(*d);
+}
+
+mhc_status mhc_post_pre(const mhc_desc* d, const void* x, const void* y, const float* H_post_in,
+                        const float* H_res_in, const float* phi, const float* bias, void* x_next,
+                        void* h, float* H_pre, float* H_post, float* H_res, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  mhc_status st = check_desc(d);
+  if (st != MHC_OK) return st;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(H_post_in) || !aligned16(H_res_in) ||
+      !aligned16(phi) || !aligned16(bias) || !aligned16(x_next) || !aligned16(h) ||
+      !aligned16(H_pre) || !aligned16(H_post) || !aligned16(H_res))
+    return MHC_ERR_INVALID_ARG;
+  const size_t b = io_bytes(d), T = (size_t)d->T, N = (size_t)d->N, D = (size_t)d->D;
+  const size_t big = T * N * D * b, small = T * D * b, cq = T * N * 4, cr = T * N * N * 4;
+  if (overlaps(x_next, big, x, big) || overlaps(x_next, big, y, small) || overlaps(h, small, x_next, big) ||
+      overlaps(h, small, x, big) || overlaps(h, small, y, small) || overlaps(H_post, cq, H_post_in, cq) ||
+      overlaps(H_post, cq, H_res_in, cr) || overlaps(H_res, cr, H_post_in, cq) ||
+      overlaps(H_res, cr, H_res_in, cr) || overlaps(H_pre, cq, H_post_in, cq) ||
+      overlaps(H_pre, cq, H_res_in, cr))
+    return MHC_ERR_INVALID_ARG;
+  if (!workspace_ok(workspace, workspace_bytes, mhc::pre_workspace_bytes(*d)))
+    return MHC_ERR_INVALID_ARG;
+  return from_hip(mhc::launch_post_pre(*d, x, y, H_post_in, H_res_in, x_next, phi, bias, h, H_pre,
+                                       H_post, H_res, workspace, stream));
+}
+
 }  // extern "C"

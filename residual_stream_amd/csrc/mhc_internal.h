@@ -25,7 +25,16 @@ size_t pre_coop_workspace_bytes(const mhc_desc& d);
 hipError_t launch_pre_coop(const mhc_desc& d, const void* x, const float* phi, const float* bias,
                            void* h, float* H_pre, float* H_post, float* H_res, void* ws,
                            hipStream_t s);
+// hc_post of one layer fused with hc_pre of the next (bf16, N = 4, D = 5120 or 2560)
+hipError_t launch_post_pre_coop(const mhc_desc& d, const void* x, const void* y, const float* H_post_in,
+                                const float* H_res_in, void* x_next, const float* phi, const float* bias,
+                                void* h, float* H_pre, float* H_post, float* H_res, void* ws,
+                                hipStream_t s);
 
+// hc_post then hc_pre on its output: fused for the split-K shapes, else the two kernels
+hipError_t launch_post_pre(const mhc_desc& d, const void* x, const void* y, const float* H_post_in,
+                           const float* H_res_in, void* x_next, const float* phi, const float* bias,
+                           void* h, float* H_pre, float* H_post, float* H_res, void* ws, hipStream_t s);
 hipError_t launch_post(const mhc_desc& d, const void* x, const void* y, const float* H_post,
                        const float* H_res, void* x_next, hipStream_t s);
 

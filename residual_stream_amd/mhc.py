@@ -31,6 +31,8 @@ ABI_FUNCTIONS = (
     "mhc_post_bwd",
     "mhc_pre_bwd_workspace_bytes",
     "mhc_pre_bwd",
+    "mhc_post_pre_workspace_bytes",
+    "mhc_post_pre",
     "mhc_status_string",
     "mhc_abi_version",
 )
@@ -74,7 +76,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.mhc_abi_version.argtypes = []
     lib.mhc_status_string.restype = ctypes.c_char_p
     lib.mhc_status_string.argtypes = [ctypes.c_int]
-    for name in ("mhc_pre_workspace_bytes", "mhc_pre_bwd_workspace_bytes"):
+    for name in ("mhc_pre_workspace_bytes", "mhc_pre_bwd_workspace_bytes", "mhc_post_pre_workspace_bytes"):
         f = getattr(lib, name)
         f.restype = ctypes.c_size_t
         f.argtypes = [_DP]
@@ -86,6 +88,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.mhc_post_bwd.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.mhc_pre_bwd.restype = ctypes.c_int
     lib.mhc_pre_bwd.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.mhc_post_pre.restype = ctypes.c_int
+    lib.mhc_post_pre.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     if path is None:
         _lib = lib
     return lib
@@ -221,6 +225,32 @@ def mhc_pre_bwd(dh, x, phi, bias, dH_post, dH_res, dx, *, iters=20, eps=1e-6,
                          _ptr(dbias), _ptr(dalpha), _ptr(workspace), nbytes, _stream(stream))
     _check(st, "mhc_pre_bwd")
     return dx, dphi, dbias, (dalpha[:3] if dalpha is not None else None)
+
+
+def mhc_post_pre(x, y, H_post, H_res, phi, bias, *, iters=20, eps=1e-6, alphas=(0.01, 0.01, 0.01),
+                 out=None, workspace=None, stream=None):
+    """hc_post of one layer fused with hc_pre of the next: x_next = H_res·x +
+    H_post ⊗ y, then hc_pre(x_next; phi, bias) of the next layer.
+
+    Returns (x_next[T,N,D], h[T,D], H_pre[T,N], H_post[T,N], H_res[T,N,N])."""
+    lib = load()
+    d = desc_for(x, iters, eps, alphas)
+    T, N, D = x.shape
+    if out is None:
+        out = (torch.empty_like(x), torch.empty((T, D), dtype=x.dtype, device=x.device),
+               torch.empty((T, N), dtype=torch.float32, device=x.device),
+               torch.empty((T, N), dtype=torch.float32, device=x.device),
+               torch.empty((T, N, N), dtype=torch.float32, device=x.device))
+    xn, h, Hp, Hq, Hr = out
+    need = lib.mhc_post_pre_workspace_bytes(ctypes.byref(d))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    nbytes = workspace.numel() if workspace is not None else 0
+    st = lib.mhc_post_pre(ctypes.byref(d), _ptr(x), _ptr(y), _ptr(_f32(H_post)), _ptr(_f32(H_res)),
+                          _ptr(_f32(phi)), _ptr(_f32(bias)), _ptr(xn), _ptr(h), _ptr(Hp), _ptr(Hq),
+                          _ptr(Hr), _ptr(workspace), nbytes, _stream(stream))
+    _check(st, "mhc_post_pre")
+    return out
 
 
 def workspace_bytes(kind: str, T: int, N: int, D: int, io: int, iters: int = 20) -> int:

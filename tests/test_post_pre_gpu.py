@@ -1,0 +1,104 @@
+"""mhc_post_pre (hc_post of one layer fused with hc_pre of the next) through
+the C ABI: equal bit for bit to mhc_post followed by mhc_pre, and within the
+bf16/fp32 tolerance of the fp64 oracle composition (hc_post, rounding of
+x_next to the I/O dtype, hc_pre)."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import mhc_oracle as O
+from residual_stream_amd import mhc
+from residual_stream_amd.inputs import make_inputs, to_io
+
+from mhc_testlib import TOL, assert_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _case(T, N, D, io, seed):
+    """Inputs of the fused call: the state x, the sublayer output y, the
+    previous layer's coefficients (a real hc_pre of x with one φ) and the next
+    layer's φ and bias (a second draw)."""
+    a = make_inputs(T, N, D, io=io, seed=seed, alpha=0.3)
+    b = make_inputs(T, N, D, io=io, seed=seed + 1000, alpha=0.3)
+    x, y = dev(a.x, io), dev(a.y, io)
+    _h, _Hp, Hq, Hr = mhc.mhc_pre(x, dev(a.phi), dev(a.bias), alphas=a.alphas)
+    return a, b, x, y, Hq, Hr
+
+
+def _both(a, b, x, y, Hq, Hr):
+    kw = dict(iters=b.iters, eps=b.eps, alphas=b.alphas)
+    fused = mhc.mhc_post_pre(x, y, Hq, Hr, dev(b.phi), dev(b.bias), **kw)
+    xn = mhc.mhc_post(x, y, Hq, Hr)
+    sep = (xn,) + tuple(mhc.mhc_pre(xn, dev(b.phi), dev(b.bias), **kw))
+    torch.cuda.synchronize()
+    return fused, sep
+
+
+def _bitwise(name, f, s):
+    assert torch.equal(f.view(torch.int16) if f.dtype == torch.bfloat16 else f,
+                       s.view(torch.int16) if s.dtype == torch.bfloat16 else s), f"{name} differs"
+
+
+NAMES = ("x_next", "h", "H_pre", "H_post", "H_res")
+
+
+@pytest.mark.parametrize("T", [1, 5, 37, 130])
+@pytest.mark.parametrize("D", [2560, 5120])
+def test_fused_equals_post_then_pre_split_k_shapes(T, D):
+    _say(f"[post_pre] bf16 N=4 D={D} T={T}")
+    fused, sep = _both(*_case(T, 4, D, "bf16", seed=T + D))
+    for name, f, s in zip(NAMES, fused, sep):
+        _bitwise(name, f, s)
+
+
+@pytest.mark.parametrize("io,N,T,D", [("bf16", 4, 37, 512), ("f32", 4, 33, 5120), ("bf16", 2, 9, 64),
+                                      ("f32", 8, 5, 40)])
+def test_fused_equals_post_then_pre_other_shapes(io, N, T, D):
+    _say(f"[post_pre] {io} N={N} D={D} T={T} (two-kernel path)")
+    fused, sep = _both(*_case(T, N, D, io, seed=3))
+    for name, f, s in zip(NAMES, fused, sep):
+        _bitwise(name, f, s)
+
+
+@pytest.mark.parametrize("io,T,D", [("bf16", 130, 5120), ("bf16", 70, 2560), ("f32", 33, 256)])
+def test_fused_matches_oracle(io, T, D):
+    _say(f"[post_pre] oracle {io} T={T} D={D}")
+    a, b, x, y, Hq, Hr = _case(T, 4, D, io, seed=21)
+    kw = dict(iters=b.iters, eps=b.eps, alphas=b.alphas)
+    xn, h, Hp2, Hq2, Hr2 = mhc.mhc_post_pre(x, y, Hq, Hr, dev(b.phi), dev(b.bias), **kw)
+    torch.cuda.synchronize()
+    tol = TOL[io]
+    ref_xn = O.hc_post(a.x, a.y, host(Hq), host(Hr))
+    assert_close("x_next", host(xn), ref_xn, tol)
+    # the next layer reads x_next as stored (rounded to the I/O dtype)
+    xn_io = to_io(ref_xn.astype(np.float32), io).astype(np.float64)
+    ref = O.hc_pre(xn_io, b.phi, b.bias, b.alphas, b.eps, b.iters)
+    assert_close("h", host(h), ref["h"], tol)
+    assert_close("H_pre", host(Hp2), ref["H_pre"], tol)
+    assert_close("H_post", host(Hq2), ref["H_post"], tol)
+    assert_close("H_res", host(Hr2), ref["H_res"], tol)
+
+
+def test_fused_full_size_equals_post_then_pre():
+    _say("[post_pre] bf16 T=4096 N=4 D=5120, all outputs bit for bit")
+    fused, sep = _both(*_case(4096, 4, 5120, "bf16", seed=99))
+    for name, f, s in zip(NAMES, fused, sep):
+        _bitwise(name, f, s)
+
+
+def test_fused_rejects_aliasing():
+    a, b, x, y, Hq, Hr = _case(5, 4, 256, "bf16", seed=1)
+    with pytest.raises(mhc.MhcError):
+        mhc.mhc_post_pre(x, y, Hq, Hr, dev(b.phi), dev(b.bias),
+                         out=(x, torch.empty_like(y), torch.empty_like(Hq), torch.empty_like(Hq),
+                              torch.empty_like(Hr)))
