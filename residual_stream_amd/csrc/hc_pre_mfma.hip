@@ -469,6 +469,7 @@ static PreConfig pick_pre(const mhc_desc& d) {
 static size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 size_t pre_workspace_bytes(const mhc_desc& d) {
+  if (pre_decode_eligible(d)) return pre_decode_workspace_bytes(d);
   const PreConfig pc = pick_pre(d);
   if (pc.tm == 0) return 0;
   const size_t own = align256((size_t)pc.nsteps * pc.cg * pc.ps * 64 * sizeof(uint4));
@@ -504,6 +505,7 @@ static hipError_t launch_mfma(const mhc_desc& d, const PreConfig& pc, const void
 hipError_t launch_pre(const mhc_desc& d, const void* x, const float* phi, const float* bias,
                       void* h, float* H_pre, float* H_post, float* H_res, void* ws,
                       hipStream_t s) {
+  if (pre_decode_eligible(d)) return launch_pre_decode(d, x, phi, bias, h, H_pre, H_post, H_res, ws, s);
   const PreConfig pc = pick_pre(d);
   if (pc.tm == 0) return launch_pre_generic(d, x, phi, bias, h, H_pre, H_post, H_res, s);
   if (pre_coop_eligible(d)) {
@@ -522,7 +524,7 @@ hipError_t launch_pre(const mhc_desc& d, const void* x, const float* phi, const 
 hipError_t launch_post_pre(const mhc_desc& d, const void* x, const void* y, const float* H_post_in,
                            const float* H_res_in, void* x_next, const float* phi, const float* bias,
                            void* h, float* H_pre, float* H_post, float* H_res, void* ws, hipStream_t s) {
-  if (pre_coop_eligible(d) && pick_pre(d).tm != 0) {
+  if (pre_coop_eligible(d) && pick_pre(d).tm != 0 && !pre_decode_eligible(d)) {
     if (launch_post_pre_coop(d, x, y, H_post_in, H_res_in, x_next, phi, bias, h, H_pre, H_post, H_res,
                              ws, s) == hipSuccess)
       return hipSuccess;

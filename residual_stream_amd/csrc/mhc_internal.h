@@ -20,6 +20,13 @@ hipError_t launch_pre(const mhc_desc& d, const void* x, const float* phi, const 
 
 // Split-K hc_pre across workgroups (bf16, N = 4, D = 5120 or 2560): groups of
 // workgroups exchange partial sums through the workspace.
+// few-token (decode-sized) hc_pre: k split across the chip, two launches
+constexpr int64_t kDecodeMaxT = 64;
+bool pre_decode_eligible(const mhc_desc& d);
+size_t pre_decode_workspace_bytes(const mhc_desc& d);
+hipError_t launch_pre_decode(const mhc_desc& d, const void* x, const float* phi, const float* bias,
+                             void* h, float* H_pre, float* H_post, float* H_res, void* ws,
+                             hipStream_t s);
 bool pre_coop_eligible(const mhc_desc& d);
 size_t pre_coop_workspace_bytes(const mhc_desc& d);
 hipError_t launch_pre_coop(const mhc_desc& d, const void* x, const float* phi, const float* bias,

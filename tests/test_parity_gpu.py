@@ -68,6 +68,23 @@ def test_tiny_workload_forward_fp32():
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("T,D", [(1, 5120), (7, 5120), (16, 5120), (17, 5120), (16, 2560), (64, 1024),
+                                 (65, 1024)])
+def test_forward_few_tokens(io, T, D):
+    # few-token path (k split across the chip, two launches) on both sides of
+    # its token limits
+    check_forward(make_inputs(T, 4, D, io=io, seed=T + D, alpha=1.0))
+
+
+def test_forward_few_tokens_deterministic():
+    inp = make_inputs(9, 4, 5120, io="bf16", seed=4, alpha=1.0)
+    a, b = gpu_forward(inp), gpu_forward(inp)
+    torch.cuda.synchronize()
+    for k in FWD_KEYS:
+        assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("N", [1, 2, 4, 8])
 @pytest.mark.parametrize("T,D", [(1, 8), (3, 24), (37, 264), (130, 1032)])
 def test_forward_shapes(io, N, T, D):
