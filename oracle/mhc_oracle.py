@@ -34,6 +34,11 @@ Readings where the pages are silent (each also listed in the design doc):
    then every column by its sum; the result is the matrix after the last
    column step.  The oracle runs the rounds as written (not the limit).
 6. The backward is the exact derivative of 1–5 (the pages give no backward).
+7. openPangu's stabilised variant ([openPangu] §5.4, first item) normalises
+   the sublayer output before H_post writes it back ("sandwich"
+   normalisation): ŷ = γ ⊙ y · (mean_d y² + eps)^(-1/2), an RMSNorm over the
+   D features of each token with a learnable weight γ[D]; then
+   x_next = H_res·x + H_post ⊗ ŷ.  Same eps as the hc_pre norm.
 
 Everything is computed in float64 from the exact input values (bf16 inputs
 arrive already upcast).  Shapes: x[T,N,D], y[T,D], phi[N·D, N²+2N],
@@ -57,6 +62,9 @@ __all__ = [
     "hc_post",
     "hc_post_bwd",
     "hc_pre_bwd",
+    "sandwich_norm",
+    "hc_post_sandwich",
+    "hc_post_sandwich_bwd",
 ]
 
 
@@ -270,3 +278,39 @@ def hc_pre_bwd(dh, x, phi, bias, dH_post, dH_res, alphas=(0.01, 0.01, 0.01),
     dx = dx + dx_flat.reshape(T, N, D)
     dphi = xf.T @ draw
     return {"dx": dx, "dphi": dphi, "dbias": dbias, "dalpha": dalpha, "dlogits": dlogits}
+
+
+def sandwich_norm(y, gamma, eps: float = 1e-6):
+    """ŷ = γ ⊙ y · r, r = (mean_d y² + eps)^(-1/2) per token ([openPangu] §5.4,
+    sandwich normalisation of the sublayer output; reading 7).  Returns
+    (ŷ[T,D], r[T])."""
+    y = _f64(y)
+    r = 1.0 / np.sqrt(np.mean(y * y, axis=1) + eps)
+    return _f64(gamma)[None, :] * y * r[:, None], r
+
+
+def hc_post_sandwich(x, y, gamma, H_post, H_res, eps: float = 1e-6) -> np.ndarray:
+    """hc_post with the sublayer output normalised before the write-back:
+    x_next = H_res·x + H_post ⊗ sandwich_norm(y)."""
+    y_hat, _ = sandwich_norm(y, gamma, eps)
+    return hc_post(x, y_hat, H_post, H_res)
+
+
+def hc_post_sandwich_bwd(dx_next, x, y, gamma, H_post, H_res, eps: float = 1e-6):
+    """Exact derivative of :func:`hc_post_sandwich`.
+
+    With g = dL/dŷ = Σ_n H_post[n]·dx_next[n] and D features:
+    dγ = Σ_t g ⊙ y·r, dy = r·(γ ⊙ g) − (r³/D)·y·Σ_d(γ ⊙ g ⊙ y);
+    dx, dH_res as in :func:`hc_post_bwd`, dH_post[n] = <dx_next[n], ŷ>.
+    Returns (dx, dy, dgamma[D], dH_post, dH_res).
+    """
+    y = _f64(y)
+    gamma = _f64(gamma)
+    T, D = y.shape
+    y_hat, r = sandwich_norm(y, gamma, eps)
+    dx, g, dH_post, dH_res = hc_post_bwd(dx_next, x, y_hat, H_post, H_res)
+    dgamma = np.sum(g * y * r[:, None], axis=0)
+    gg = gamma[None, :] * g
+    s = np.sum(gg * y, axis=1)
+    dy = r[:, None] * gg - (r ** 3 / D)[:, None] * y * s[:, None]
+    return dx, dy, dgamma, dH_post, dH_res
