@@ -39,6 +39,13 @@ Readings where the pages are silent (each also listed in the design doc):
    normalisation): ŷ = γ ⊙ y · (mean_d y² + eps)^(-1/2), an RMSNorm over the
    D features of each token with a learnable weight γ[D]; then
    x_next = H_res·x + H_post ⊗ ŷ.  Same eps as the hc_pre norm.
+8. The block-level post-norm of the same list (second item: after the first
+   layer and every fifth layer) is an RMSNorm of each token's whole N-stream
+   state, over the flattened N·D vector like the hc_pre norm, with a learnable
+   weight w[N·D]: x_next ← w ⊙ z · (mean_k z² + eps)^(-1/2), z the write-back
+   result.  It is applied to the state the write-back produces.
+9. A learnable weight w[N·D] on the hc_pre RMSNorm, x̄ = w ⊙ x·rstd, enters
+   only the logits (h collapses the raw streams).
 
 Everything is computed in float64 from the exact input values (bf16 inputs
 arrive already upcast).  Shapes: x[T,N,D], y[T,D], phi[N·D, N²+2N],
@@ -65,6 +72,12 @@ __all__ = [
     "sandwich_norm",
     "hc_post_sandwich",
     "hc_post_sandwich_bwd",
+    "rms_norm",
+    "rms_norm_bwd",
+    "hc_post_stable",
+    "hc_post_stable_bwd",
+    "hc_pre_weighted",
+    "hc_pre_weighted_bwd",
 ]
 
 
@@ -314,3 +327,116 @@ def hc_post_sandwich_bwd(dx_next, x, y, gamma, H_post, H_res, eps: float = 1e-6)
     s = np.sum(gg * y, axis=1)
     dy = r[:, None] * gg - (r ** 3 / D)[:, None] * y * s[:, None]
     return dx, dy, dgamma, dH_post, dH_res
+
+
+def rms_norm(v, weight, eps: float = 1e-6):
+    """Row-wise RMSNorm with a learnable weight: out = w ⊙ v · r,
+    r = (mean over the row of v² + eps)^(-1/2).  v[T,F], weight[F].  Returns
+    (out[T,F], r[T]).  Readings 7 and 8 use it over D (sublayer output) and
+    over N·D (the whole state)."""
+    v = _f64(v)
+    r = 1.0 / np.sqrt(np.mean(v * v, axis=1) + eps)
+    return _f64(weight)[None, :] * v * r[:, None], r
+
+
+def rms_norm_bwd(dout, v, weight, eps: float = 1e-6):
+    """Exact derivative of :func:`rms_norm`: with u = w ⊙ dout and F features,
+    dv = r·u − (r³/F)·v·Σ(u ⊙ v) and dw = Σ_t dout ⊙ v·r.  Returns (dv, dw)."""
+    v = _f64(v)
+    dout = _f64(dout)
+    F = v.shape[1]
+    _, r = rms_norm(v, weight, eps)
+    u = _f64(weight)[None, :] * dout
+    s = np.sum(u * v, axis=1)
+    dv = r[:, None] * u - (r ** 3 / F)[:, None] * v * s[:, None]
+    dw = np.sum(dout * v * r[:, None], axis=0)
+    return dv, dw
+
+
+def hc_post_stable(x, y, H_post, H_res, y_weight=None, out_weight=None, eps: float = 1e-6):
+    """The stabilised write-back of [openPangu] §5.4 (readings 7 and 8):
+    ŷ = rms_norm(y, y_weight) (sandwich norm; ŷ = y when y_weight is None),
+    z = H_res·x + H_post ⊗ ŷ, x_next = rms_norm(z over N·D, out_weight) (block
+    post-norm; x_next = z when out_weight is None).  Returns x_next[T,N,D]."""
+    x = _f64(x)
+    T, N, D = x.shape
+    y_hat = _f64(y) if y_weight is None else rms_norm(y, y_weight, eps)[0]
+    z = hc_post(x, y_hat, H_post, H_res)
+    if out_weight is None:
+        return z
+    return rms_norm(z.reshape(T, N * D), out_weight, eps)[0].reshape(T, N, D)
+
+
+def hc_post_stable_bwd(dx_next, x, y, H_post, H_res, y_weight=None, out_weight=None,
+                       eps: float = 1e-6):
+    """Exact derivative of :func:`hc_post_stable`, by the chain rule through
+    its three steps.  Returns dict(dx, dy, dH_post, dH_res, dy_weight,
+    dout_weight); a weight's gradient is None when the weight is None."""
+    x = _f64(x)
+    T, N, D = x.shape
+    y = _f64(y)
+    y_hat = y if y_weight is None else rms_norm(y, y_weight, eps)[0]
+    g = _f64(dx_next)
+    dout_weight = None
+    if out_weight is not None:
+        z = hc_post(x, y_hat, H_post, H_res)
+        dz, dout_weight = rms_norm_bwd(g.reshape(T, N * D), z.reshape(T, N * D), out_weight, eps)
+        g = dz.reshape(T, N, D)
+    dx, dy_hat, dH_post, dH_res = hc_post_bwd(g, x, y_hat, H_post, H_res)
+    dy_weight = None
+    dy = dy_hat
+    if y_weight is not None:
+        dy, dy_weight = rms_norm_bwd(dy_hat, y, y_weight, eps)
+    return {"dx": dx, "dy": dy, "dH_post": dH_post, "dH_res": dH_res,
+            "dy_weight": dy_weight, "dout_weight": dout_weight}
+
+
+def hc_pre_weighted(x, norm_weight, phi, bias, alphas=(0.01, 0.01, 0.01), eps: float = 1e-6,
+                    iters: int = 20):
+    """hc_pre with a learnable weight on its RMSNorm (reading 9):
+    x̄ = w ⊙ x·rstd over the flattened N·D state, ℓ = α_g·(x̄·φ) + b, then the
+    gates, Sinkhorn and the collapse h = Σ_n H_pre[n]·x[n] of raw x as in
+    :func:`hc_pre`.  Returns the same dict as :func:`hc_pre`."""
+    x = _f64(x)
+    T, N, D = x.shape
+    xbar, rstd = rms_norm(x.reshape(T, N * D), norm_weight, eps)
+    q = xbar @ _f64(phi)
+    l_pre, l_post, l_res = split_logits(q, bias, alphas, N)
+    H_pre, H_post = gates(l_pre, l_post)
+    H_res = sinkhorn(np.exp(l_res), iters)
+    h = np.einsum("tn,tnd->td", H_pre, x)
+    return {"h": h, "H_pre": H_pre, "H_post": H_post, "H_res": H_res, "rstd": rstd,
+            "l_pre": l_pre, "l_post": l_post, "l_res": l_res}
+
+
+def hc_pre_weighted_bwd(dh, x, norm_weight, phi, bias, dH_post, dH_res,
+                        alphas=(0.01, 0.01, 0.01), eps: float = 1e-6, iters: int = 20):
+    """Exact derivative of :func:`hc_pre_weighted`, recomputing from x.
+    Returns dict(dx (hc_pre's part), dphi, dbias, dalpha, dnorm_weight)."""
+    x = _f64(x)
+    T, N, D = x.shape
+    K = N * D
+    phi = _f64(phi)
+    xf = x.reshape(T, K)
+    xbar, _ = rms_norm(xf, norm_weight, eps)
+    q = xbar @ phi
+    l_pre, l_post, l_res = split_logits(q, bias, alphas, N)
+    H_pre, H_post = gates(l_pre, l_post)
+    M0 = np.exp(l_res)
+    _, trace = sinkhorn_trace(M0, iters)
+
+    dh = _f64(dh)
+    dH_pre = np.einsum("td,tnd->tn", dh, x)
+    dx = H_pre[:, :, None] * dh[:, None, :]
+    s_post = H_post / 2.0
+    dl_pre = dH_pre * H_pre * (1.0 - H_pre)
+    dl_post = _f64(dH_post) * 2.0 * s_post * (1.0 - s_post)
+    dl_res = sinkhorn_bwd(trace, dH_res) * M0
+    dlogits = np.concatenate([dl_pre, dl_post, dl_res.reshape(T, N * N)], axis=1)
+    dq = dlogits * _alpha_vector(N, alphas)[None, :]
+    groups = [slice(0, N), slice(N, 2 * N), slice(2 * N, 2 * N + N * N)]
+    dalpha = np.array([np.sum(dlogits[:, g] * q[:, g]) for g in groups])
+    dphi = xbar.T @ dq
+    dxf, dw = rms_norm_bwd(dq @ phi.T, xf, norm_weight, eps)
+    return {"dx": dx + dxf.reshape(T, N, D), "dphi": dphi, "dbias": dlogits.sum(axis=0),
+            "dalpha": dalpha, "dnorm_weight": dw}
