@@ -14,6 +14,8 @@
  *   hc_post  — same section (roles of the maps) and the Ascend mHC Triton
  *              article's definition paragraph: x_next[n] = Σ_m H_res[n,m]·x[m]
  *              + H_post[n]·y.
+ *   stabilised write-back — the sandwich norm and block post-norm of
+ *              openPangu's variant (§5.4); see mhc_post_stable.
  *   backward — the exact derivative of the above; hc_pre's backward recomputes
  *              norm, logits and Sinkhorn from x (the Ascend article's
  *              intra-layer recompute paragraph keeps only the hc_pre input and
@@ -53,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MHC_ABI_VERSION 1
+#define MHC_ABI_VERSION 2
 
 typedef enum mhc_dtype { MHC_F32 = 0, MHC_BF16 = 1 } mhc_dtype;
 
@@ -149,6 +151,41 @@ mhc_status mhc_post_pre(const mhc_desc* desc, const void* x, const void* y, cons
                         const float* H_res_in, const float* phi, const float* bias, void* x_next,
                         void* h, float* H_pre, float* H_post, float* H_res, void* workspace,
                         size_t workspace_bytes, hipStream_t stream);
+
+/* openPangu's stabilised write-back (openPangu 2.0 analysis, §5.4, first two
+ * items), per token:
+ *   ŷ      = y_weight ⊙ y · (mean_d y² + eps)^(-1/2)   sandwich norm of the
+ *            sublayer output before H_post writes it back (ŷ = y if y_weight
+ *            is NULL)
+ *   z      = H_res·x + H_post ⊗ ŷ                        (as mhc_post)
+ *   x_next = out_weight ⊙ z · (mean z² + eps)^(-1/2)     block post-norm over
+ *            the token's flattened N·D state (x_next = z if out_weight is NULL)
+ * y_weight[D] and out_weight[N·D] are fp32; eps is desc->eps, the hc_pre norm's.
+ * With both weights NULL this is mhc_post.  With a weight, N·⌈D/5120⌉ must be
+ * at most 4 (D ≤ 5120 at N = 4, 10240 at N = 2, 20480 at N = 1), else
+ * MHC_ERR_UNSUPPORTED.  The rest of the mhc_post contract applies. */
+mhc_status mhc_post_stable(const mhc_desc* desc, const void* x, const void* y, const float* y_weight,
+                           const float* H_post, const float* H_res, const float* out_weight,
+                           void* x_next, hipStream_t stream);
+
+/* Bytes of device workspace mhc_post_stable_bwd needs for the given weights
+ * (nonzero flags: that weight is present); 0 for an invalid descriptor or
+ * when neither is. */
+size_t mhc_post_stable_bwd_workspace_bytes(const mhc_desc* desc, int with_y_weight, int with_out_weight);
+
+/* Backward of mhc_post_stable, recomputing ŷ, z and both norms from x and y.
+ * Writes dx (I/O dtype, overwritten: mhc_pre_bwd then adds hc_pre's part), dy
+ * (I/O dtype), dH_post, dH_res (fp32), and the weight gradients summed over
+ * the tokens: dy_weight[D] (required if and only if y_weight is given) and
+ * dout_weight[N·D] (likewise for out_weight), fp32, overwritten.  The
+ * workspace holds mhc_post_stable_bwd_workspace_bytes bytes, 256-byte
+ * aligned; its contents on entry are ignored.  With both weights NULL this is
+ * mhc_post_bwd (no workspace).  Shape limits as for mhc_post_stable. */
+mhc_status mhc_post_stable_bwd(const mhc_desc* desc, const void* dx_next, const void* x, const void* y,
+                               const float* y_weight, const float* H_post, const float* H_res,
+                               const float* out_weight, void* dx, void* dy, float* dy_weight,
+                               float* dout_weight, float* dH_post, float* dH_res, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
 
 /* MHC_ABI_VERSION of the built library. */
 int mhc_abi_version(void);

@@ -19,7 +19,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmhc.so")
 
 SOURCES = ["mhc_api.cpp", "hc_pre.hip", "hc_pre_mfma.hip", "hc_post.hip", "hc_bwd.hip",
-           "hc_pre_bwd_mfma.hip", "hc_pre_coop.hip", "hc_pre_decode.hip"]
+           "hc_pre_bwd_mfma.hip", "hc_pre_coop.hip", "hc_pre_decode.hip",
+           "hc_post_stable.hip"]
 
 ARCH = "gfx950"
 # Packed-fp32 VALU instructions are switched off for every device pass.

@@ -191,4 +191,66 @@ mhc_status mhc_post_pre(const mhc_desc* d, const void* x, const void* y, const f
                                        H_post, H_res, workspace, stream));
 }
 
+size_t mhc_post_stable_bwd_workspace_bytes(const mhc_desc* d, int with_y_weight, int with_out_weight) {
+  if (check_desc(d) != MHC_OK) return 0;
+  if (!with_y_weight && !with_out_weight) return 0;
+  if (!mhc::post_stable_supported(*d)) return 0;
+  return mhc::post_stable_bwd_workspace_bytes(*d, with_y_weight != 0, with_out_weight != 0);
+}
+
+mhc_status mhc_post_stable(const mhc_desc* d, const void* x, const void* y, const float* y_weight,
+                           const float* H_post, const float* H_res, const float* out_weight,
+                           void* x_next, hipStream_t stream) {
+  mhc_status st = check_desc(d);
+  if (st != MHC_OK) return st;
+  if ((y_weight != nullptr || out_weight != nullptr) && !mhc::post_stable_supported(*d))
+    return MHC_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(H_post) || !aligned16(H_res) || !aligned16(x_next))
+    return MHC_ERR_INVALID_ARG;
+  if ((y_weight != nullptr && !aligned16(y_weight)) || (out_weight != nullptr && !aligned16(out_weight)))
+    return MHC_ERR_INVALID_ARG;
+  const size_t b = io_bytes(d), T = (size_t)d->T, N = (size_t)d->N, D = (size_t)d->D;
+  const size_t big = T * N * D * b, small = T * D * b;
+  if (overlaps(x_next, big, x, big) || overlaps(x_next, big, y, small) ||
+      (y_weight != nullptr && overlaps(x_next, big, y_weight, D * 4)) ||
+      (out_weight != nullptr && overlaps(x_next, big, out_weight, N * D * 4)))
+    return MHC_ERR_INVALID_ARG;
+  return from_hip(mhc::launch_post_stable(*d, x, y, y_weight, H_post, H_res, out_weight, x_next, stream));
+}
+
+mhc_status mhc_post_stable_bwd(const mhc_desc* d, const void* dx_next, const void* x, const void* y,
+                               const float* y_weight, const float* H_post, const float* H_res,
+                               const float* out_weight, void* dx, void* dy, float* dy_weight,
+                               float* dout_weight, float* dH_post, float* dH_res, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  mhc_status st = check_desc(d);
+  if (st != MHC_OK) return st;
+  const bool sw = y_weight != nullptr, pn = out_weight != nullptr;
+  if ((sw || pn) && !mhc::post_stable_supported(*d)) return MHC_ERR_UNSUPPORTED;
+  if (sw != (dy_weight != nullptr) || pn != (dout_weight != nullptr)) return MHC_ERR_INVALID_ARG;
+  if (!aligned16(dx_next) || !aligned16(x) || !aligned16(y) || !aligned16(H_post) ||
+      !aligned16(H_res) || !aligned16(dx) || !aligned16(dy) || !aligned16(dH_post) ||
+      !aligned16(dH_res))
+    return MHC_ERR_INVALID_ARG;
+  if ((sw && (!aligned16(y_weight) || !aligned16(dy_weight))) ||
+      (pn && (!aligned16(out_weight) || !aligned16(dout_weight))))
+    return MHC_ERR_INVALID_ARG;
+  const size_t b = io_bytes(d), T = (size_t)d->T, N = (size_t)d->N, D = (size_t)d->D;
+  const size_t big = T * N * D * b, small = T * D * b;
+  if (overlaps(dx, big, dx_next, big) || overlaps(dx, big, x, big) || overlaps(dx, big, y, small) ||
+      overlaps(dy, small, dx_next, big) || overlaps(dy, small, x, big) || overlaps(dy, small, dx, big) ||
+      overlaps(dy, small, y, small))
+    return MHC_ERR_INVALID_ARG;
+  const size_t need = mhc_post_stable_bwd_workspace_bytes(d, sw, pn);
+  if (!workspace_ok(workspace, workspace_bytes, need)) return MHC_ERR_INVALID_ARG;
+  if (need != 0) {
+    const size_t part = need;
+    if ((sw && overlaps(dy_weight, D * 4, workspace, part)) || (pn && overlaps(dout_weight, N * D * 4, workspace, part)))
+      return MHC_ERR_INVALID_ARG;
+  }
+  return from_hip(mhc::launch_post_stable_bwd(*d, dx_next, x, y, y_weight, H_post, H_res, out_weight, dx,
+                                              dy, dy_weight, dout_weight, dH_post, dH_res, workspace,
+                                              stream));
+}
+
 }  // extern "C"

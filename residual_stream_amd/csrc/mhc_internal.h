@@ -49,6 +49,18 @@ hipError_t launch_post_bwd(const mhc_desc& d, const void* dxn, const void* x, co
                            const float* H_post, const float* H_res, void* dx, void* dy,
                            float* dH_post, float* dH_res, hipStream_t s);
 
+// openPangu's stabilised write-back (sandwich norm of y with weight wy, block
+// post-norm of the state with weight wx; a null weight turns its norm off)
+bool post_stable_supported(const mhc_desc& d);
+size_t post_stable_bwd_workspace_bytes(const mhc_desc& d, bool sw, bool pn);
+hipError_t launch_post_stable(const mhc_desc& d, const void* x, const void* y, const float* wy,
+                              const float* H_post, const float* H_res, const float* wx, void* x_next,
+                              hipStream_t s);
+hipError_t launch_post_stable_bwd(const mhc_desc& d, const void* dxn, const void* x, const void* y,
+                                  const float* wy, const float* H_post, const float* H_res,
+                                  const float* wx, void* dx, void* dy, float* dwy, float* dwx,
+                                  float* dH_post, float* dH_res, void* ws, hipStream_t s);
+
 size_t pre_bwd_workspace_bytes(const mhc_desc& d);
 
 // Matrix-core backward of hc_pre (bf16, N = 4, D % 256 == 0); leaves the

@@ -13,6 +13,13 @@ activations are drawn directly in float32, phi and bias in float64):
 * bias[N²+2N] ~ N(0, 0.1)  (variance 0.1)
 * dh[T,D] ~ N(0,1), dx_next[T,N,D] ~ N(0,1)   — upstream gradients (optional)
 
+Inputs of the write-back calls that are not drawn above come from
+``make_coefficients`` (a separate generator, so that the write-back can be
+checked without running hc_pre): H_post[T,N] ~ U(0, 2) and H_res[T,N,N] ~
+U(0, 1), in the ranges the maps take, with no normalisation; and from
+``make_norm_weights``: learnable norm weights ~ U(0.5, 1.5), y_weight[D] and
+out_weight[N·D].
+
 x, y, dh and dx_next are rounded to the I/O dtype (fp32, or bf16 with
 round-to-nearest-even); phi and bias are always fp32.  Every array is returned
 as float32 numpy holding exactly the stored values, so upcasting to float64 is
@@ -104,6 +111,21 @@ def make_inputs(T: int, N: int, D: int, io: str = IO_F32, seed: int = 0,
     alphas = tuple(float(a) for a in alpha) if isinstance(alpha, (tuple, list)) else (float(alpha),) * 3
     return MhcInputs(T=T, N=N, D=D, io=io, x=x, y=y, phi=phi, bias=bias, alphas=alphas,
                      eps=float(eps), iters=int(iters), dh=dh, dx_next=dxn)
+
+
+def make_coefficients(T: int, N: int, seed: int = 0):
+    """Seeded H_post[T,N] ~ U(0,2) and H_res[T,N,N] ~ U(0,1), float32."""
+    rng = np.random.default_rng(seed)
+    H_post = rng.uniform(0.0, 2.0, (T, N)).astype(np.float32)
+    H_res = rng.uniform(0.0, 1.0, (T, N, N)).astype(np.float32)
+    return H_post, H_res
+
+
+def make_norm_weights(N: int, D: int, seed: int = 0):
+    """Seeded learnable norm weights ~ U(0.5, 1.5): y_weight[D], out_weight[N·D], float32."""
+    rng = np.random.default_rng(seed)
+    return (rng.uniform(0.5, 1.5, D).astype(np.float32),
+            rng.uniform(0.5, 1.5, N * D).astype(np.float32))
 
 
 # Named workloads: shapes of the pages' training activations (mHC with 4

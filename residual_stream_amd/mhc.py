@@ -33,6 +33,9 @@ ABI_FUNCTIONS = (
     "mhc_pre_bwd",
     "mhc_post_pre_workspace_bytes",
     "mhc_post_pre",
+    "mhc_post_stable",
+    "mhc_post_stable_bwd_workspace_bytes",
+    "mhc_post_stable_bwd",
     "mhc_status_string",
     "mhc_abi_version",
 )
@@ -90,6 +93,12 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.mhc_pre_bwd.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.mhc_post_pre.restype = ctypes.c_int
     lib.mhc_post_pre.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.mhc_post_stable.restype = ctypes.c_int
+    lib.mhc_post_stable.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.mhc_post_stable_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.mhc_post_stable_bwd_workspace_bytes.argtypes = [_DP, ctypes.c_int, ctypes.c_int]
+    lib.mhc_post_stable_bwd.restype = ctypes.c_int
+    lib.mhc_post_stable_bwd.argtypes = [_DP] + [_P] * 14 + [ctypes.c_size_t, _P]
     if path is None:
         _lib = lib
     return lib
@@ -259,3 +268,47 @@ def workspace_bytes(kind: str, T: int, N: int, D: int, io: int, iters: int = 20)
     d = make_desc(T, N, D, io, iters)
     f = lib.mhc_pre_workspace_bytes if kind == "pre" else lib.mhc_pre_bwd_workspace_bytes
     return int(f(ctypes.byref(d)))
+
+
+def mhc_post_stable(x, y, H_post, H_res, *, y_weight=None, out_weight=None, eps=1e-6, out=None,
+                    stream=None):
+    """Stabilised write-back: sandwich norm of y (weight y_weight[D]) before
+    H_post writes it back and block post-norm of the state (weight
+    out_weight[N·D]) after; either weight may be None.  Returns x_next."""
+    lib = load()
+    d = desc_for(x, eps=eps)
+    if out is None:
+        out = torch.empty_like(x)
+    yw = None if y_weight is None else _f32(y_weight)
+    ow = None if out_weight is None else _f32(out_weight)
+    st = lib.mhc_post_stable(ctypes.byref(d), _ptr(x), _ptr(y), _ptr(yw), _ptr(_f32(H_post)),
+                             _ptr(_f32(H_res)), _ptr(ow), _ptr(out), _stream(stream))
+    _check(st, "mhc_post_stable")
+    return out
+
+
+def mhc_post_stable_bwd(dx_next, x, y, H_post, H_res, *, y_weight=None, out_weight=None, eps=1e-6,
+                        out=None, workspace=None, stream=None):
+    """Backward of :func:`mhc_post_stable`.  Returns (dx, dy, dH_post, dH_res,
+    dy_weight or None, dout_weight or None)."""
+    lib = load()
+    d = desc_for(x, eps=eps)
+    T, N, D = x.shape
+    sw, pn = y_weight is not None, out_weight is not None
+    if out is None:
+        f32 = dict(dtype=torch.float32, device=x.device)
+        out = (torch.empty_like(x), torch.empty_like(y), torch.empty((T, N), **f32),
+               torch.empty((T, N, N), **f32), torch.empty(D, **f32) if sw else None,
+               torch.empty(N * D, **f32) if pn else None)
+    dx, dy, dHp, dHr, dyw, dow = out
+    need = lib.mhc_post_stable_bwd_workspace_bytes(ctypes.byref(d), int(sw), int(pn))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    nbytes = workspace.numel() if workspace is not None else 0
+    st = lib.mhc_post_stable_bwd(
+        ctypes.byref(d), _ptr(dx_next), _ptr(x), _ptr(y),
+        _ptr(None if y_weight is None else _f32(y_weight)), _ptr(_f32(H_post)), _ptr(_f32(H_res)),
+        _ptr(None if out_weight is None else _f32(out_weight)), _ptr(dx), _ptr(dy), _ptr(dyw),
+        _ptr(dow), _ptr(dHp), _ptr(dHr), _ptr(workspace), nbytes, _stream(stream))
+    _check(st, "mhc_post_stable_bwd")
+    return out

@@ -30,6 +30,25 @@ def test_header_declares_the_binding_surface():
     assert _declared_functions() == sorted(mhc.ABI_FUNCTIONS)
 
 
+def _declared_arity():
+    """Number of parameters of each declared function (``(void)`` counts 0)."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for name, params in re.findall(r"\b(mhc_[a-z_0-9]+)\s*\(([^)]*)\)\s*;", text):
+        p = params.strip()
+        out[name] = 0 if p in ("", "void") else p.count(",") + 1
+    return out
+
+
+def test_binding_signatures_match_the_header(lib):
+    # ctypes does not check a call against the C prototype; the argtypes the
+    # binding sets must have the header's arity
+    arity = _declared_arity()
+    assert sorted(arity) == _declared_functions()
+    for name, n in arity.items():
+        assert len(getattr(lib, name).argtypes) == n, name
+
+
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name

@@ -1,9 +1,10 @@
 """MHCBlock (torch.autograd wiring of the four C-ABI calls) against the fp64
 oracle: x_next, and the gradients of a linear loss with respect to x, φ, b and
-α, through a sublayer y = F(h).  The sublayer runs in torch on the GPU; the
-oracle reference is fed the very h, y and dh values the GPU path produced at
-the sublayer boundary (the sublayer is not part of mHC), so the comparison is
-of the mHC steps alone, to the kernels' tolerance."""
+α, through a sublayer y = c ⊙ h with a fixed seeded vector c.  The oracle
+composes the same steps from the seeded inputs alone (hc_pre, y = c ⊙ h,
+hc_post; then hc_post_bwd, dh = c ⊙ dy, hc_pre_bwd), in fp64 without the
+rounding of h, y and dh to the I/O dtype that the GPU path stores; that
+rounding stays inside the tolerance."""
 
 from __future__ import annotations
 
@@ -14,9 +15,9 @@ import pytest
 import torch
 
 from oracle import mhc_oracle as O
-from residual_stream_amd.inputs import make_inputs
+from residual_stream_amd.inputs import make_inputs, make_norm_weights
 
-from mhc_testlib import TOL, assert_close, dev, host, tdtype
+from mhc_testlib import TOL, assert_close, dev, host
 
 pytestmark = pytest.mark.gpu
 
@@ -36,43 +37,40 @@ class _Scale(torch.nn.Module):
         return h * self.c
 
 
-def _run(inp, recompute, seed=7):
+def _scale_vector(inp):
+    return make_norm_weights(inp.N, inp.D, seed=7)[0]  # U(0.5, 1.5)[D]
+
+
+def _run(inp, recompute):
     from residual_stream_amd.autograd import MHCBlock
 
     io = inp.io
-    rng = np.random.default_rng(seed)
-    c = dev(rng.uniform(0.5, 1.5, inp.D).astype(np.float32), io)
-    g = dev(rng.standard_normal((inp.T, inp.N, inp.D)).astype(np.float32), io)
+    c = dev(_scale_vector(inp), io)
+    g = dev(inp.dx_next, io)
     block = MHCBlock(_Scale(c), inp.N, inp.D, iters=inp.iters, eps=inp.eps, alpha=inp.alphas,
                      train_alpha=True, recompute=recompute)
     with torch.no_grad():
         block.phi.copy_(dev(inp.phi))
         block.bias.copy_(dev(inp.bias))
     x = dev(inp.x, io).requires_grad_(True)
-    # capture the sublayer boundary values for the oracle
-    seen = {}
-    block.sublayer.register_forward_hook(lambda m, a, out: seen.update(h=a[0].detach(), y=out.detach()))
     xn = block(x)
     (xn.float() * g.float()).sum().backward()
     torch.cuda.synchronize()
-    return block, x, xn, g, c, seen
+    return block, x, xn
 
 
 @pytest.mark.parametrize("io,T,D", [("bf16", 70, 256), ("f32", 33, 64), ("bf16", 5, 512)])
 def test_block_matches_oracle(io, T, D):
     _say(f"[autograd] io={io} T={T} D={D}")
-    inp = make_inputs(T, 4, D, io=io, seed=11, alpha=0.3)
-    block, x, xn, g, c, seen = _run(inp, recompute=False)
-    h_gpu, y_gpu = host(seen["h"]), host(seen["y"])
+    inp = make_inputs(T, 4, D, io=io, seed=11, alpha=0.3, grads=True)
+    block, x, xn = _run(inp, recompute=False)
+    c = _scale_vector(inp).astype(np.float64)
     ref = O.hc_pre(inp.x, inp.phi, inp.bias, inp.alphas, inp.eps, inp.iters)
+    y = ref["h"] * c[None, :]
     tol = TOL[io]
-    assert_close("h", h_gpu, ref["h"], tol)
-    assert_close("x_next", host(xn), O.hc_post(inp.x, y_gpu, ref["H_post"], ref["H_res"]), tol)
-    # backward reference: the same dxn; dy through the oracle; dh = dy ⊙ c rounded as torch does
-    gn = host(g)
-    dx_post, dy, dHq, dHr = O.hc_post_bwd(gn, inp.x, y_gpu, ref["H_post"], ref["H_res"])
-    dy_io = torch.from_numpy(dy.astype(np.float32)).to(tdtype(io)).cuda()
-    dh = host(dy_io * c)
+    assert_close("x_next", host(xn), O.hc_post(inp.x, y, ref["H_post"], ref["H_res"]), tol)
+    dx_post, dy, dHq, dHr = O.hc_post_bwd(inp.dx_next, inp.x, y, ref["H_post"], ref["H_res"])
+    dh = dy * c[None, :]
     pre = O.hc_pre_bwd(dh, inp.x, inp.phi, inp.bias, dHq, dHr, inp.alphas, inp.eps, inp.iters)
     assert_close("dx", host(x.grad), dx_post + pre["dx"], tol)
     assert_close("dphi", host(block.phi.grad), pre["dphi"], tol)
@@ -82,7 +80,7 @@ def test_block_matches_oracle(io, T, D):
 
 def test_recompute_gives_identical_gradients():
     _say("[autograd] recompute on/off, bf16 T=70 D=256")
-    inp = make_inputs(70, 4, 256, io="bf16", seed=5, alpha=0.3)
+    inp = make_inputs(70, 4, 256, io="bf16", seed=5, alpha=0.3, grads=True)
     a = _run(inp, recompute=False)
     b = _run(inp, recompute=True)
     assert torch.equal(a[2], b[2])

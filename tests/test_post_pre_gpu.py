@@ -13,7 +13,7 @@ import torch
 
 from oracle import mhc_oracle as O
 from residual_stream_amd import mhc
-from residual_stream_amd.inputs import make_inputs, to_io
+from residual_stream_amd.inputs import make_coefficients, make_inputs, to_io
 
 from mhc_testlib import TOL, assert_close, dev, host
 
@@ -25,14 +25,14 @@ def _say(msg):
 
 
 def _case(T, N, D, io, seed):
-    """Inputs of the fused call: the state x, the sublayer output y, the
-    previous layer's coefficients (a real hc_pre of x with one φ) and the next
-    layer's φ and bias (a second draw)."""
+    """Inputs of the fused call, all seeded: the state x, the sublayer output
+    y, the previous layer's coefficients H_post / H_res (drawn in their
+    ranges), and the next layer's φ and bias (a second draw)."""
     a = make_inputs(T, N, D, io=io, seed=seed, alpha=0.3)
     b = make_inputs(T, N, D, io=io, seed=seed + 1000, alpha=0.3)
     x, y = dev(a.x, io), dev(a.y, io)
-    _h, _Hp, Hq, Hr = mhc.mhc_pre(x, dev(a.phi), dev(a.bias), alphas=a.alphas)
-    return a, b, x, y, Hq, Hr
+    Hq, Hr = make_coefficients(T, N, seed=seed + 2000)
+    return a, b, x, y, dev(Hq), dev(Hr)
 
 
 def _both(a, b, x, y, Hq, Hr):
@@ -78,7 +78,8 @@ def test_fused_matches_oracle(io, T, D):
     xn, h, Hp2, Hq2, Hr2 = mhc.mhc_post_pre(x, y, Hq, Hr, dev(b.phi), dev(b.bias), **kw)
     torch.cuda.synchronize()
     tol = TOL[io]
-    ref_xn = O.hc_post(a.x, a.y, host(Hq), host(Hr))
+    Hq_ref, Hr_ref = make_coefficients(T, 4, seed=21 + 2000)
+    ref_xn = O.hc_post(a.x, a.y, Hq_ref, Hr_ref)
     assert_close("x_next", host(xn), ref_xn, tol)
     # the next layer reads x_next as stored (rounded to the I/O dtype)
     xn_io = to_io(ref_xn.astype(np.float32), io).astype(np.float64)
