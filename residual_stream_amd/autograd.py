@@ -20,8 +20,19 @@ backward writes its part of dx, and the hc_pre backward adds its own to it in
 place.  The hc_post node therefore hands its dx to the hc_pre node of the same
 block instead of returning it; the hc_pre node returns the total.
 
-Every step runs in the library's kernels; this module only wires them into
-autograd.  It needs a GPU and the built library, like the binding.
+openPangu's stabilised variant (openPangu 2.0 analysis, §5.4) is available
+through three switches: ``sandwich_norm`` (an RMSNorm with a learnable weight
+on y before H_post writes it back), ``post_norm`` (an RMSNorm with a learnable
+weight over each token's flattened N·D state after the write-back: the
+block-level post-norm, which a model enables on the first block and every
+fifth) and ``pre_norm_weight`` (a learnable weight on the hc_pre RMSNorm).
+The first two run in ``mhc_post_stable`` and its backward.  The hc_pre weight
+w only scales the normalised state before the projection, so it is folded
+into the projection's rows, φ' = diag(w)·φ, a [N·D, N²+2N] parameter product
+computed once per step; the per-token work stays in the kernels.
+
+Every per-token step runs in the library's kernels; this module only wires
+them into autograd.  It needs a GPU and the built library, like the binding.
 """
 
 from __future__ import annotations
@@ -76,18 +87,29 @@ class _Pre(torch.autograd.Function):
 
 class _Post(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, x, y, H_post, H_res, handoff):
-        x_next = mhc.mhc_post(x, y, H_post, H_res)
-        ctx.save_for_backward(x, y, H_post, H_res)
+    def forward(ctx, x, y, H_post, H_res, y_weight, out_weight, eps, handoff):
+        if y_weight is None and out_weight is None:
+            x_next = mhc.mhc_post(x, y, H_post, H_res)
+        else:
+            x_next = mhc.mhc_post_stable(x, y, H_post, H_res, y_weight=y_weight,
+                                         out_weight=out_weight, eps=eps)
+        ctx.save_for_backward(x, y, H_post, H_res, y_weight, out_weight)
+        ctx.eps = eps
         ctx.handoff = handoff
         return x_next
 
     @staticmethod
     def backward(ctx, dx_next):
-        x, y, H_post, H_res = ctx.saved_tensors
-        dx, dy, dHq, dHr = mhc.mhc_post_bwd(dx_next.contiguous(), x, y, H_post, H_res)
+        x, y, H_post, H_res, y_weight, out_weight = ctx.saved_tensors
+        if y_weight is None and out_weight is None:
+            dx, dy, dHq, dHr = mhc.mhc_post_bwd(dx_next.contiguous(), x, y, H_post, H_res)
+            dyw = dow = None
+        else:
+            dx, dy, dHq, dHr, dyw, dow = mhc.mhc_post_stable_bwd(
+                dx_next.contiguous(), x, y, H_post, H_res, y_weight=y_weight,
+                out_weight=out_weight, eps=ctx.eps)
         ctx.handoff.dx = dx  # the hc_pre backward of this block adds to it
-        return None, dy, dHq, dHr, None
+        return None, dy, dHq, dHr, dyw, dow, None, None
 
 
 class MHCBlock(torch.nn.Module):
@@ -96,13 +118,16 @@ class MHCBlock(torch.nn.Module):
 
     Parameters: φ[N·D, N²+2N] and b[N²+2N] (fp32, on the GPU) and the three gate
     scalars α = (α_pre, α_post, α_res) as a host tensor (their values are
-    launch parameters; their gradient comes back from the GPU).  x is
-    [T, N, D] or [B, S, N, D], fp32 or bf16, on the GPU.
+    launch parameters; their gradient comes back from the GPU); with the
+    stabilisation switches also y_weight[D], out_weight[N·D] and
+    pre_weight[N·D] (fp32, initialised to one).  x is [T, N, D] or
+    [B, S, N, D], fp32 or bf16, on the GPU.
     """
 
     def __init__(self, sublayer: torch.nn.Module, n_streams: int, hidden: int, *,
                  iters: int = 20, eps: float = 1e-6, alpha=(0.01, 0.01, 0.01),
-                 train_alpha: bool = False, recompute: bool = False, device="cuda"):
+                 train_alpha: bool = False, recompute: bool = False, sandwich_norm: bool = False,
+                 post_norm: bool = False, pre_norm_weight: bool = False, device="cuda"):
         super().__init__()
         N, D = n_streams, hidden
         C = N * N + 2 * N
@@ -112,9 +137,19 @@ class MHCBlock(torch.nn.Module):
         self.bias = torch.nn.Parameter(torch.zeros(C, device=device))
         self.alpha = torch.nn.Parameter(torch.tensor(alpha, dtype=torch.float32),
                                         requires_grad=train_alpha)
+        ones = lambda n: torch.nn.Parameter(torch.ones(n, device=device))  # noqa: E731
+        self.y_weight = ones(D) if sandwich_norm else None
+        self.out_weight = ones(N * D) if post_norm else None
+        self.pre_weight = ones(N * D) if pre_norm_weight else None
+
+    def _phi(self):
+        if self.pre_weight is None:
+            return self.phi
+        return (self.pre_weight[:, None] * self.phi).contiguous()
 
     def _pre_sub(self, x, handoff):
-        h, _Hp, Hq, Hr = _Pre.apply(x, self.phi, self.bias, self.alpha, self.iters, self.eps, handoff)
+        h, _Hp, Hq, Hr = _Pre.apply(x, self._phi(), self.bias, self.alpha, self.iters, self.eps,
+                                    handoff)
         return self.sublayer(h), Hq, Hr
 
     def forward(self, x):
@@ -129,5 +164,6 @@ class MHCBlock(torch.nn.Module):
             y, Hq, Hr = checkpoint(self._pre_sub, x, handoff, use_reentrant=False)
         else:
             y, Hq, Hr = self._pre_sub(x, handoff)
-        x_next = _Post.apply(x, y.contiguous(), Hq, Hr, handoff)
+        x_next = _Post.apply(x, y.contiguous(), Hq, Hr, self.y_weight, self.out_weight, self.eps,
+                             handoff)
         return x_next.reshape(shape)

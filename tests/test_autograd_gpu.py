@@ -101,3 +101,48 @@ def test_batched_state_shape():
     assert out.shape == x.shape
     flat = block(x.reshape(12, 4, 64))
     assert torch.equal(out.reshape(12, 4, 64), flat)
+
+
+@pytest.mark.parametrize("io,T,D", [("bf16", 70, 256), ("f32", 33, 64)])
+def test_stabilised_block_matches_oracle(io, T, D):
+    # openPangu's variant: sandwich norm, block post-norm and a weighted hc_pre
+    # norm, all three weights trained; the oracle composes hc_pre_weighted,
+    # y = c ⊙ h and hc_post_stable, then their backward passes
+    _say(f"[autograd] stabilised block io={io} T={T} D={D}")
+    from residual_stream_amd.autograd import MHCBlock
+
+    N = 4
+    inp = make_inputs(T, N, D, io=io, seed=13, alpha=0.3, grads=True)
+    wy, wx = make_norm_weights(N, D, seed=14)
+    wp = make_norm_weights(N, D, seed=15)[1]
+    c = _scale_vector(inp)
+    block = MHCBlock(_Scale(dev(c, io)), N, D, iters=inp.iters, eps=inp.eps, alpha=inp.alphas,
+                     train_alpha=True, sandwich_norm=True, post_norm=True, pre_norm_weight=True)
+    with torch.no_grad():
+        block.phi.copy_(dev(inp.phi))
+        block.bias.copy_(dev(inp.bias))
+        block.y_weight.copy_(dev(wy))
+        block.out_weight.copy_(dev(wx))
+        block.pre_weight.copy_(dev(wp))
+    x = dev(inp.x, io).requires_grad_(True)
+    xn = block(x)
+    (xn.float() * dev(inp.dx_next, io).float()).sum().backward()
+    torch.cuda.synchronize()
+
+    c = c.astype(np.float64)
+    pre = O.hc_pre_weighted(inp.x, wp, inp.phi, inp.bias, inp.alphas, inp.eps, inp.iters)
+    y = pre["h"] * c[None, :]
+    tol = TOL[io]
+    assert_close("x_next", host(xn),
+                 O.hc_post_stable(inp.x, y, pre["H_post"], pre["H_res"], wy, wx, inp.eps), tol)
+    post = O.hc_post_stable_bwd(inp.dx_next, inp.x, y, pre["H_post"], pre["H_res"], wy, wx, inp.eps)
+    dh = post["dy"] * c[None, :]
+    pb = O.hc_pre_weighted_bwd(dh, inp.x, wp, inp.phi, inp.bias, post["dH_post"], post["dH_res"],
+                               inp.alphas, inp.eps, inp.iters)
+    assert_close("dx", host(x.grad), post["dx"] + pb["dx"], tol)
+    assert_close("dphi", host(block.phi.grad), pb["dphi"], tol)
+    assert_close("dbias", host(block.bias.grad), pb["dbias"], tol)
+    assert_close("dalpha", block.alpha.grad.double().numpy(), pb["dalpha"], tol)
+    assert_close("dy_weight", host(block.y_weight.grad), post["dy_weight"], tol)
+    assert_close("dout_weight", host(block.out_weight.grad), post["dout_weight"], tol)
+    assert_close("dpre_weight", host(block.pre_weight.grad), pb["dnorm_weight"], tol)
