@@ -53,6 +53,12 @@ def algo_bytes(T, N, D, io):
         "mhc_pre_bwd": T * (D * e + 3 * K * e + coef) + 2 * phi,
         # hc_post(l) + hc_pre(l+1): x, y, H_post/H_res in; x_next, h, H out
         "mhc_post_pre": T * (K * e + D * e + coef + K * e + D * e + C * 4) + phi,
+        # stabilised write-back: as mhc_post / mhc_post_bwd plus the norm
+        # weights read (and their gradients written) once per call
+        "mhc_post_stable_sw": T * (K * e + D * e + coef + K * e) + D * 4,
+        "mhc_post_stable_both": T * (K * e + D * e + coef + K * e) + (D + K) * 4,
+        "mhc_post_stable_bwd_sw": T * (3 * K * e + 2 * D * e + 2 * coef) + 2 * D * 4,
+        "mhc_post_stable_bwd_both": T * (3 * K * e + 2 * D * e + 2 * coef) + 2 * (D + K) * 4,
     }
 
 
@@ -63,6 +69,10 @@ CALL_KERNELS = {
     "mhc_post": ["hc_post_generic"],
     "mhc_post_bwd": ["hc_post_bwd_generic"],
     "mhc_pre_bwd": ["bwd_proj_kernel", "bwd_coef_kernel", "bwd_dx_kernel", "dphi_bias_sum_kernel"],
+    "mhc_post_stable_sw": ["post_stable_fwd"],
+    "mhc_post_stable_both": ["post_stable_fwd"],
+    "mhc_post_stable_bwd_sw": ["post_stable_bwd", "stable_wsum"],
+    "mhc_post_stable_bwd_both": ["post_stable_bwd", "stable_wsum"],
 }
 
 
@@ -136,7 +146,7 @@ def main():
     import torch
 
     from residual_stream_amd import mhc
-    from residual_stream_amd.inputs import make_inputs
+    from residual_stream_amd.inputs import make_inputs, make_norm_weights
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -187,6 +197,10 @@ def main():
         st["dphi"] = torch.empty((K, C), dtype=torch.float32, device=dev)
         st["dbias"] = torch.empty((C,), dtype=torch.float32, device=dev)
         st["dalpha"] = torch.empty((4,), dtype=torch.float32, device=dev)
+        wy, wx = make_norm_weights(N, D, seed=args.seed + 10 + s)
+        st["wy"], st["wx"] = t(wy), t(wx)
+        st["dwy"] = torch.empty((D,), dtype=torch.float32, device=dev)
+        st["dwx"] = torch.empty((K,), dtype=torch.float32, device=dev)
         sets.append(st)
         del inp
     ws_pre = mhc.workspace_bytes("pre", T, N, D, mhc.MHC_BF16 if io == "bf16" else mhc.MHC_F32)
@@ -195,6 +209,13 @@ def main():
     ws_bwd_t = torch.empty(ws_bwd, dtype=torch.uint8, device=dev)
 
     stream = torch.cuda.current_stream()
+    stab_ok = N * ((D + 5119) // 5120) <= 4  # shapes the stabilised write-back supports
+    ws_stab = {}
+    if stab_ok:
+        for pn in (False, True):
+            n = mhc.workspace_bytes("post_stable_bwd", T, N, D, mhc.MHC_BF16 if io == "bf16" else mhc.MHC_F32,
+                                    y_weight=True, out_weight=pn)
+            ws_stab[(True, pn)] = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
 
     def call_pre(st):
         mhc.mhc_pre(st["x"], st["phi"], st["bias"], out=(st["h"], st["Hp"], st["Hq"], st["Hr"]),
@@ -215,6 +236,18 @@ def main():
         mhc.mhc_pre_bwd(st["dh"], st["x"], st["phi"], st["bias"], st["dHp"], st["dHr"], st["dx"],
                         out=(st["dphi"], st["dbias"], st["dalpha"]), workspace=ws_bwd_t,
                         stream=stream, **kw)
+
+    def call_stable(st, pn):
+        mhc.mhc_post_stable(st["x"], st["y"], st["Hq"], st["Hr"], y_weight=st["wy"],
+                            out_weight=st["wx"] if pn else None, eps=kw["eps"], out=st["xn"],
+                            stream=stream)
+
+    def call_stable_bwd(st, pn):
+        mhc.mhc_post_stable_bwd(st["dxn"], st["x"], st["y"], st["Hq"], st["Hr"], y_weight=st["wy"],
+                                out_weight=st["wx"] if pn else None, eps=kw["eps"],
+                                out=(st["dx"], st["dy"], st["dHp"], st["dHr"], st["dwy"],
+                                     st["dwx"] if pn else None),
+                                workspace=ws_stab[(True, pn)], stream=stream)
 
     calls = [("mhc_pre", call_pre), ("mhc_post", call_post), ("mhc_post_bwd", call_post_bwd),
              ("mhc_pre_bwd", call_pre_bwd)]
@@ -293,6 +326,30 @@ def main():
     pp_ts = sorted(a.elapsed_time(b) for a, b in evs)
     pp_ms = sum(pp_ts) / len(pp_ts)
 
+    # openPangu's stabilised write-back (sandwich norm on every layer, the
+    # block post-norm added on every fifth), timed like the fused call
+    stabilised = {}
+    if stab_ok:
+        for name, f in (("mhc_post_stable_sw", lambda st: call_stable(st, False)),
+                        ("mhc_post_stable_both", lambda st: call_stable(st, True)),
+                        ("mhc_post_stable_bwd_sw", lambda st: call_stable_bwd(st, False)),
+                        ("mhc_post_stable_bwd_both", lambda st: call_stable_bwd(st, True))):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+            for i in range(args.steps):
+                evs[i][0].record(stream)
+                f(sets[i % 2])
+                evs[i][1].record(stream)
+                for _, f2 in calls:
+                    f2(sets[(i + 1) % 2])
+            torch.cuda.synchronize()
+            ts = sorted(a.elapsed_time(b) for a, b in evs)
+            avg = sum(ts) / len(ts)
+            gbps = ab[name] / (avg * 1e-3) / 1e9
+            stabilised[name] = {"avg_us": avg * 1e3, "median_us": ts[len(ts) // 2] * 1e3,
+                                "algo_bytes": ab[name], "gbps": gbps, "frac_of_peak": gbps / HBM_PEAK_GBPS,
+                                "kernels": CALL_KERNELS[name]}
+
     dom = max(per_call, key=lambda k: per_call[k]["avg_us"])
     src_hash = kernel_source_hash()
     traffic = load_traffic(dom, src_hash)
@@ -327,6 +384,7 @@ def main():
                            "gbps": ab["mhc_post_pre"] / (pp_ms * 1e-3) / 1e9,
                            "frac_of_peak": ab["mhc_post_pre"] / (pp_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                            "separate_us": per_call["mhc_post"]["avg_us"] + per_call["mhc_pre"]["avg_us"]},
+        "stabilised_write_back": stabilised,
         "roofline": {"kernel": dom, "kernels": CALL_KERNELS.get(dom, []), "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,

@@ -24,8 +24,8 @@
 //   dy = r_y·w_y⊙g − (r_y³/D)·Σ(w_y⊙g⊙y)·y                 (sandwich on; else g)
 //   dw_y = Σ_t r_y·g⊙y,              dw_x = Σ_t r_z·dx_next⊙z
 // The weight gradients are sums over tokens: a fixed grid of G workgroups
-// walks the tokens t ≡ b (mod G), each keeping its share of dw in registers,
-// and writes one row of partial sums; a second kernel adds the G rows in
+// walks the tokens t ≡ b (mod G), each keeping its share of dw (dw_x in LDS,
+// dw_y in registers), and writes one row of partial sums; a second kernel adds the G rows in
 // order.
 #include "mhc_device.h"
 #include "mhc_internal.h"
@@ -312,9 +312,14 @@ __global__ __launch_bounds__(kMaxThreads) void post_stable_bwd(
   const int nthr = blockDim.x;
   const int K = N * D;
   const uint32_t rowD = (uint32_t)D * B;  // bytes of one stream row
+  // dw_x partial sums of this thread live in LDS, not in registers: slot
+  // (j, n, half) of thread i at accx_s[((j·N + n)·2 + half)·nthr + i], so a
+  // wave's 16-byte accesses are contiguous.  Dynamic LDS of
+  // accx_lds_bytes(N, CPT, nthr): N·CPT ≤ 4 makes it at most 80 KB.
+  extern __shared__ float4 accx_s[];
   int d0[CPT];
   bool ok[CPT];
-  float wyr[CPT][8], accy[CPT][8], accx[CPT][N][8];
+  float wyr[CPT][8], accy[CPT][8];
 #pragma unroll
   for (int j = 0; j < CPT; ++j) {
     d0[j] = 8 * (j * nthr + (int)threadIdx.x);
@@ -323,10 +328,12 @@ __global__ __launch_bounds__(kMaxThreads) void post_stable_bwd(
     for (int e = 0; e < 8; ++e) {
       wyr[j][e] = 0.f;
       accy[j][e] = 0.f;
-#pragma unroll
-      for (int n = 0; n < N; ++n) accx[j][n][e] = 0.f;
     }
     if (SW && ok[j]) load_w8(wy, d0[j], wyr[j]);
+    if constexpr (PN) {
+#pragma unroll
+      for (int q = 0; q < N * 2; ++q) accx_s[(j * N * 2 + q) * nthr + threadIdx.x] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
   }
   // Every access below is a raw buffer access: a scalar descriptor per token
   // row, one 32-bit lane offset per chunk and the stream offset as a scalar
@@ -413,15 +420,22 @@ __global__ __launch_bounds__(kMaxThreads) void post_stable_bwd(
       for (int j = 0; j < CPT; ++j) {
 #pragma unroll
         for (int n = 0; n < N; ++n) {
-          float w[8];
+          float w[8], a[8];
           load_w8(rwx, vw[j], (uint32_t)(n * D) * 4u, w);
+          float4& s0 = accx_s[((j * N + n) * 2) * nthr + threadIdx.x];
+          float4& s1 = accx_s[((j * N + n) * 2 + 1) * nthr + threadIdx.x];
+          const float4 a0 = s0, a1 = s1;
+          a[0] = a0.x; a[1] = a0.y; a[2] = a0.z; a[3] = a0.w;
+          a[4] = a1.x; a[5] = a1.y; a[6] = a1.z; a[7] = a1.w;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float zz = z_at<N, IO, SW>(hp[n], hr[n], xr[j], yr[j][e], ry, wyr[j][e], e);
             const float d = dr[j][n][e];
-            accx[j][n][e] += (d * zz) * rz;
+            a[e] += (d * zz) * rz;
             gz[j][n][e] = rz * (w[e] * d) - c * zz;
           }
+          s0 = make_float4(a[0], a[1], a[2], a[3]);
+          s1 = make_float4(a[4], a[5], a[6], a[7]);
         }
       }
 #pragma unroll
@@ -512,7 +526,11 @@ __global__ __launch_bounds__(kMaxThreads) void post_stable_bwd(
     if constexpr (SW) store_f8(row + d0[j], accy[j]);
     if constexpr (PN) {
 #pragma unroll
-      for (int n = 0; n < N; ++n) store_f8(row + (SW ? D : 0) + n * D + d0[j], accx[j][n]);
+      for (int n = 0; n < N; ++n) {
+        float4* q = reinterpret_cast<float4*>(row + (SW ? D : 0) + n * D + d0[j]);
+        q[0] = accx_s[((j * N + n) * 2) * nthr + threadIdx.x];
+        q[1] = accx_s[((j * N + n) * 2 + 1) * nthr + threadIdx.x];
+      }
     }
   }
 }
@@ -597,6 +615,11 @@ bool dispatch(int N, int io, int cpt, bool sw, bool pn, F&& f) {
   return done;
 }
 
+// Dynamic LDS of the backward: the dw_x partial sums of every thread.
+size_t accx_lds_bytes(int N, int cpt, int nthr, bool pn) {
+  return pn ? (size_t)cpt * N * 2 * nthr * sizeof(float4) : 0;
+}
+
 // Workgroups of the backward: as many as fit on the device at once, at most
 // one per token.
 int bwd_grid(const mhc_desc& d, bool sw, bool pn) {
@@ -607,7 +630,9 @@ int bwd_grid(const mhc_desc& d, bool sw, bool pn) {
     const void* k = reinterpret_cast<const void*>(
         &post_stable_bwd<decltype(n_)::value, decltype(io_)::value, decltype(c_)::value,
                          decltype(sw_)::value, decltype(pn_)::value>);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, s.nthr, 0) != hipSuccess) per_cu = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, s.nthr,
+                                                     accx_lds_bytes(d.N, s.cpt, s.nthr, pn)) != hipSuccess)
+      per_cu = 1;
   });
   if (per_cu < 1) per_cu = 1;
   const int64_t g = (int64_t)per_cu * device_cu_count();
@@ -659,7 +684,8 @@ hipError_t launch_post_stable_bwd(const mhc_desc& d, const void* dxn, const void
   const bool ok = stab::dispatch(d.N, d.io, sh.cpt, sw, pn, [&](auto n_, auto io_, auto c_, auto sw_, auto pn_) {
     hipLaunchKernelGGL((stab::post_stable_bwd<decltype(n_)::value, decltype(io_)::value, decltype(c_)::value,
                                               decltype(sw_)::value, decltype(pn_)::value>),
-                       dim3((unsigned)G), dim3(sh.nthr), 0, s, dxn, x, y, wy, H_post, H_res, wx, dx, dy,
+                       dim3((unsigned)G), dim3(sh.nthr), stab::accx_lds_bytes(d.N, sh.cpt, sh.nthr, pn), s,
+                       dxn, x, y, wy, H_post, H_res, wx, dx, dy,
                        dH_post, dH_res, part, d.T, d.D, d.eps);
   });
   if (!ok) return hipErrorInvalidValue;

@@ -262,11 +262,16 @@ def mhc_post_pre(x, y, H_post, H_res, phi, bias, *, iters=20, eps=1e-6, alphas=(
     return out
 
 
-def workspace_bytes(kind: str, T: int, N: int, D: int, io: int, iters: int = 20) -> int:
-    """Workspace size for 'pre' or 'pre_bwd' (host-only query)."""
+def workspace_bytes(kind: str, T: int, N: int, D: int, io: int, iters: int = 20, *,
+                    y_weight: bool = False, out_weight: bool = False) -> int:
+    """Workspace size (host-only query) for 'pre', 'pre_bwd', 'post_pre' or
+    'post_stable_bwd' (with the given norm weights present)."""
     lib = load()
     d = make_desc(T, N, D, io, iters)
-    f = lib.mhc_pre_workspace_bytes if kind == "pre" else lib.mhc_pre_bwd_workspace_bytes
+    if kind == "post_stable_bwd":
+        return int(lib.mhc_post_stable_bwd_workspace_bytes(ctypes.byref(d), int(y_weight), int(out_weight)))
+    f = {"pre": lib.mhc_pre_workspace_bytes, "pre_bwd": lib.mhc_pre_bwd_workspace_bytes,
+         "post_pre": lib.mhc_post_pre_workspace_bytes}[kind]
     return int(f(ctypes.byref(d)))
 
 
