@@ -69,10 +69,10 @@ CALL_KERNELS = {
     "mhc_post": ["hc_post_generic"],
     "mhc_post_bwd": ["hc_post_bwd_generic"],
     "mhc_pre_bwd": ["bwd_proj_kernel", "bwd_coef_kernel", "bwd_dx_kernel", "dphi_bias_sum_kernel"],
-    "mhc_post_stable_sw": ["post_stable_fwd"],
-    "mhc_post_stable_both": ["post_stable_fwd"],
-    "mhc_post_stable_bwd_sw": ["post_stable_bwd", "stable_wsum"],
-    "mhc_post_stable_bwd_both": ["post_stable_bwd", "stable_wsum"],
+    "mhc_post_stable_sw": ["post_stable_fwd<4, 1, 1, true, false>"],
+    "mhc_post_stable_both": ["post_stable_fwd<4, 1, 1, true, true>"],
+    "mhc_post_stable_bwd_sw": ["post_stable_bwd<4, 1, 1, true, false>", "stable_wsum[grid=81920]"],
+    "mhc_post_stable_bwd_both": ["post_stable_bwd<4, 1, 1, true, true>", "stable_wsum[grid=409600]"],
 }
 
 
