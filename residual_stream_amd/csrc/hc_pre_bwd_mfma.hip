@@ -51,15 +51,21 @@ __device__ __forceinline__ f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
 }
 
 // ------------------------------------------------------------- pass 1 ---
-// Persistent split-K reduction.  A workgroup = W waves, each owning one 32-d
-// block (all four streams) of a slice of 32·W d, walks a contiguous token range
-// in 16-token blocks.  Its φ B fragments stay in VGPRs; x and dh stream three
-// blocks ahead (a ring of four register slots, loaded through row-bounded
-// buffer descriptors); the projections go to the matrix cores, the sums of
-// squares and <dh, x[n]> to v_dot2_f32_bf16.  The waves' partials meet in LDS
-// (double-buffered, one barrier per block) and one summed record per (slice,
-// token) goes to the workspace.
-constexpr int kPRing = 4;    // register slots of x/dh per wave
+// Persistent split-K reduction.  A workgroup = W waves walks a contiguous
+// token range in 16-token blocks for one slice of 32·W d (all four streams).
+// Global traffic is linear: thread i moves the 16-byte pieces i, i + 64W, …
+// of a block (x piece q: token q / (16W), stream (q / 4W) mod 4, 8-d chunk
+// q mod 4W; dh piece i: token i / 4W, chunk i mod 4W), so each wave access
+// reads runs of 64W bytes of every token row (640 B at W = 10) instead of the
+// 64-byte pieces a matrix-core fragment covers.  Pieces stream three blocks
+// ahead in a ring of four register slots (row-bounded buffer descriptors) and
+// meet the matrix cores in LDS: each block is written to one of two padded
+// tiles, then every wave reads its fragments (its own 32-d block) from there.
+// Wave w projects its block with the φ B fragments it keeps in VGPRs; sums of
+// squares and <dh, x[n]> go to v_dot2_f32_bf16.  The waves' partials meet in
+// LDS and one summed record per (slice, token) goes to the workspace, a block
+// late (after the next block's barrier): one barrier per block.
+constexpr int kPRing = 4;    // register slots of x/dh pieces per thread
 constexpr int kPRec = 29;    // record: p[24], ss, dhp[4]
 
 template <int CTRL>
@@ -75,12 +81,23 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 }
 
 template <int W>
+struct ProjTile {
+  static constexpr int kCh = 4 * W;                  // 8-d chunks of a stream row in the slice
+  static constexpr int kXRow = kN * kCh * 16 + 16;   // bytes per token of the x tile (+16: banks)
+  static constexpr int kHRow = kCh * 16 + 16;        // bytes per token of the dh tile
+  static constexpr int kBytes = 16 * (kXRow + kHRow);
+};
+
+template <int W>
 __global__ __launch_bounds__(64 * W, 1) void bwd_proj_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ dh, const float* __restrict__ phi,
     float* __restrict__ part, int64_t T, int D, int64_t R) {
   constexpr int kThr = 64 * W;
   constexpr int kSl = 32 * W;  // d per slice
+  using TL = ProjTile<W>;
+  constexpr int kCh = TL::kCh;
   __shared__ __align__(16) float red[2][W][16][kPartStride];
+  __shared__ __align__(16) char tile[2][TL::kBytes];
   // Token indices are 32-bit (T < 2^31): uniform compares then stay scalar,
   // and no VGPR temporary (which could alias an in-flight load) is needed.
   const int slice = blockIdx.x;
@@ -91,9 +108,21 @@ __global__ __launch_bounds__(64 * W, 1) void bwd_proj_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int row = lane & 15, g = lane >> 4;
-  const int d0 = slice * kSl + wave * 32;  // this wave's d block
 
-  uint4 xs[kPRing][kN], hs[kPRing];
+  // this thread's pieces: global byte offsets within a block and LDS offsets
+  uint32_t gx[4], lx[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int q = threadIdx.x + j * kThr;
+    const int tk = q / (kN * kCh), n = (q / kCh) % kN, c = q % kCh;
+    gx[j] = (uint32_t)((tk * K + n * D + slice * kSl + 8 * c) * 2);
+    lx[j] = (uint32_t)(tk * TL::kXRow + (n * kCh + c) * 16);
+  }
+  const int htk = threadIdx.x / kCh, hc = threadIdx.x % kCh;
+  const uint32_t gh = (uint32_t)((htk * D + slice * kSl + 8 * hc) * 2);
+  const uint32_t lh = (uint32_t)(16 * TL::kXRow + htk * TL::kHRow + hc * 16);
+
+  uint4 xs[kPRing][4], hs[kPRing];
   auto load_blk = [&](int b, auto slot_c) {
     constexpr int SL = decltype(slot_c)::value;
     const int t0 = tb + 16 * b;
@@ -102,8 +131,8 @@ __global__ __launch_bounds__(64 * W, 1) void bwd_proj_kernel(
     const auto rx = make_rsrc(x + (int64_t)base * K, (uint32_t)rows * (uint32_t)K * 2u);
     const auto rh = make_rsrc(dh + (int64_t)base * D, (uint32_t)rows * (uint32_t)D * 2u);
 #pragma unroll
-    for (int n = 0; n < kN; ++n) xs[SL][n] = ld16(rx, (uint32_t)(((row * kN + n) * D + d0 + 8 * g) * 2));
-    hs[SL] = ld16(rh, (uint32_t)((row * D + d0 + 8 * g) * 2));
+    for (int j = 0; j < 4; ++j) xs[SL][j] = ld16(rx, gx[j]);
+    hs[SL] = ld16(rh, gh);
   };
 
   // The first three blocks' loads go out first, so that x and dh stream while
@@ -155,16 +184,39 @@ __global__ __launch_bounds__(64 * W, 1) void bwd_proj_kernel(
     }
   }
 
+  // record of block b: the W waves' partials summed in a fixed order; rows
+  // past the range fall outside the store descriptor
+  auto record = [&](int b) {
+    const int t0 = tb + 16 * b;
+    const int rows = b < nblk ? ((te - t0) < 16 ? (te - t0) : 16) : 0;
+    const auto rp = make_rsrc(part + ((int64_t)slice * T + (rows > 0 ? t0 : 0)) * kPartStride,
+                              (uint32_t)rows * kPartStride * 4u);
+    static_assert(16 * kPRec <= kThr, "one record value per thread");
+    if (threadIdx.x < 16 * kPRec) {
+      const int tk = threadIdx.x / kPRec, c = threadIdx.x % kPRec;
+      float v = red[b & 1][0][tk][c];
+#pragma unroll
+      for (int w = 1; w < W; ++w) v += red[b & 1][w][tk][c];
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rp, (tk * kPartStride + c) * 4, 0, 0);
+    }
+  };
+
   auto block = [&](int b, auto slot_c) {
     constexpr int SL = decltype(slot_c)::value;
     load_blk(b + kPRing - 1, std::integral_constant<int, (SL + kPRing - 1) % kPRing>{});
     __builtin_amdgcn_sched_barrier(0);
+    char* tl = tile[b & 1];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(tl + lx[j]) = xs[SL][j];
+    *reinterpret_cast<uint4*>(tl + lh) = hs[SL];
+    __syncthreads();
+    if (b > 0) record(b - 1);
     f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     float ss = 0.f, dhp[kN] = {0.f, 0.f, 0.f, 0.f};
-    const uint4 hv = hs[SL];
+    const uint4 hv = *reinterpret_cast<const uint4*>(tl + 16 * TL::kXRow + row * TL::kHRow + (4 * wave + g) * 16);
 #pragma unroll
     for (int n = 0; n < kN; ++n) {
-      const uint4 a = xs[SL][n];
+      const uint4 a = *reinterpret_cast<const uint4*>(tl + row * TL::kXRow + (n * kCh + 4 * wave + g) * 16);
       acc0 = mfma(a, bfr[n][0], acc0);
       acc1 = mfma(a, bfr[n][1], acc1);
       ss = dot2(a.x, a.x, ss);
@@ -196,32 +248,22 @@ __global__ __launch_bounds__(64 * W, 1) void bwd_proj_kernel(
 #pragma unroll
       for (int n = 0; n < kN; ++n) rw[row][kC + 1 + n] = dhp[n];
     }
-    __syncthreads();
-    // record of each token: the W waves summed in a fixed order; rows past
-    // the range fall outside the store descriptor
-    const int t0 = tb + 16 * b;
-    const int rows = b < nblk ? ((te - t0) < 16 ? (te - t0) : 16) : 0;
-    const auto rp = make_rsrc(part + ((int64_t)slice * T + (rows > 0 ? t0 : 0)) * kPartStride,
-                              (uint32_t)rows * kPartStride * 4u);
-    static_assert(16 * kPRec <= kThr, "one record value per thread");
-    if (threadIdx.x < 16 * kPRec) {
-      const int tk = threadIdx.x / kPRec, c = threadIdx.x % kPRec;
-      float v = red[b & 1][0][tk][c];
-#pragma unroll
-      for (int w = 1; w < W; ++w) v += red[b & 1][w][tk][c];
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rp, (tk * kPartStride + c) * 4, 0, 0);
-    }
   };
 
   // Whole ring turns only (blocks past the range load and store nothing): a
   // loop with a single exit keeps each slot in the same registers on every
   // pass, so the wait counts stay exact across the back edge.
   static_assert(kPRing == 4, "unroll below");
-  for (int b = 0; b < nblk; b += kPRing) {
+  int b = 0;
+  for (; b < nblk; b += kPRing) {
     block(b, std::integral_constant<int, 0>{});
     block(b + 1, std::integral_constant<int, 1>{});
     block(b + 2, std::integral_constant<int, 2>{});
     block(b + 3, std::integral_constant<int, 3>{});
+  }
+  if (b > 0) {
+    __syncthreads();
+    record(b - 1);
   }
 }
 
