@@ -65,7 +65,16 @@ __device__ __forceinline__ f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
 // squares and <dh, x[n]> go to v_dot2_f32_bf16.  The waves' partials meet in
 // LDS and one summed record per (slice, token) goes to the workspace, a block
 // late (after the next block's barrier): one barrier per block.
-constexpr int kPRing = 4;    // register slots of x/dh pieces per thread
+constexpr int kPRing = 4;  // register slots of x/dh pieces per thread (a fifth spills at W = 10)
+
+// f(integral_constant<int, i>) for i = I .. N − 1, in order.
+template <int I, int N, typename F>
+__device__ __forceinline__ void unroll_slots(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    unroll_slots<I + 1, N>(f);
+  }
+}
 constexpr int kPRec = 29;    // record: p[24], ss, dhp[4]
 
 template <int CTRL>
@@ -135,16 +144,14 @@ __global__ __launch_bounds__(64 * W, 1) void bwd_proj_kernel(
     hs[SL] = ld16(rh, gh);
   };
 
-  // The first three blocks' loads go out first, so that x and dh stream while
-  // φ is staged (vector memory completes in order: the φ loads below arrive
-  // after them, and the block loop is entered with nothing outstanding).
+  // The first kPRing − 1 blocks' loads go out first, so that x and dh stream
+  // while φ is staged (vector memory completes in order: the φ loads below
+  // arrive after them, and the block loop is entered with nothing outstanding).
   // (kept in issue order: the wait counts in the loop assume slot 0 oldest)
-  load_blk(0, std::integral_constant<int, 0>{});
-  __builtin_amdgcn_sched_barrier(0);
-  load_blk(1, std::integral_constant<int, 1>{});
-  __builtin_amdgcn_sched_barrier(0);
-  load_blk(2, std::integral_constant<int, 2>{});
-  __builtin_amdgcn_sched_barrier(0);
+  unroll_slots<0, kPRing - 1>([&](auto sl) {
+    load_blk(decltype(sl)::value, sl);
+    __builtin_amdgcn_sched_barrier(0);
+  });
 
   // φ: stream by stream through LDS (the red buffer), all global loads of a
   // thread issued before the first LDS write
@@ -253,14 +260,8 @@ __global__ __launch_bounds__(64 * W, 1) void bwd_proj_kernel(
   // Whole ring turns only (blocks past the range load and store nothing): a
   // loop with a single exit keeps each slot in the same registers on every
   // pass, so the wait counts stay exact across the back edge.
-  static_assert(kPRing == 4, "unroll below");
   int b = 0;
-  for (; b < nblk; b += kPRing) {
-    block(b, std::integral_constant<int, 0>{});
-    block(b + 1, std::integral_constant<int, 1>{});
-    block(b + 2, std::integral_constant<int, 2>{});
-    block(b + 3, std::integral_constant<int, 3>{});
-  }
+  for (; b < nblk; b += kPRing) unroll_slots<0, kPRing>([&](auto sl) { block(b + decltype(sl)::value, sl); });
   if (b > 0) {
     __syncthreads();
     record(b - 1);
