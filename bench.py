@@ -10,8 +10,10 @@ Infinity Cache left warm by the previous one.
 
 Prints one JSON line.  `value` is tokens/s of the full step; the forward pair
 (hc_pre + hc_post, the HBM-roofline headline) is reported in "forward";
-"roofline" describes the kernel that takes the most time in the step, timed
-with HIP events on its own stream; "cpu_baseline" times the fp64 oracle on the
+"roofline" describes the single kernel that takes the most time in the step
+(a call that launches one kernel, timed with HIP events on its stream), and
+"largest_call" the call that takes the most time (the four-kernel hc_pre
+backward); "cpu_baseline" times the fp64 oracle on the
 host cores.
 """
 
@@ -350,7 +352,13 @@ def main():
                                 "algo_bytes": ab[name], "gbps": gbps, "frac_of_peak": gbps / HBM_PEAK_GBPS,
                                 "kernels": CALL_KERNELS[name]}
 
-    dom = max(per_call, key=lambda k: per_call[k]["avg_us"])
+    # roofline: the single-kernel call that takes the most time in the step,
+    # so that its event time is one kernel's duration (the rocprofv3 summary
+    # lists the same kernel); the multi-kernel hc_pre backward is reported
+    # beside it as the largest call
+    single = [k for k in per_call if len(CALL_KERNELS[k]) == 1]
+    dom = max(single, key=lambda k: per_call[k]["avg_us"])
+    big = max(per_call, key=lambda k: per_call[k]["avg_us"])
     src_hash = kernel_source_hash()
     traffic = load_traffic(dom, src_hash)
     achieved = per_call[dom]["gbps"]
@@ -385,10 +393,13 @@ def main():
                            "frac_of_peak": ab["mhc_post_pre"] / (pp_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                            "separate_us": per_call["mhc_post"]["avg_us"] + per_call["mhc_pre"]["avg_us"]},
         "stabilised_write_back": stabilised,
-        "roofline": {"kernel": dom, "kernels": CALL_KERNELS.get(dom, []), "bound": "hbm",
+        "roofline": {"kernel": CALL_KERNELS[dom][0], "call": dom, "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "algo_bytes_per_launch": ab[dom], "avg_us": per_call[dom]["avg_us"]},
+        "largest_call": {"call": big, "kernels": CALL_KERNELS[big], "avg_us": per_call[big]["avg_us"],
+                         "achieved": per_call[big]["gbps"], "frac": per_call[big]["gbps"] / HBM_PEAK_GBPS,
+                         "traffic": load_traffic(big, src_hash), "algo_bytes_per_launch": ab[big]},
         "kernel_source_hash": src_hash,
     }
     if not args.no_cpu_baseline:
