@@ -11,7 +11,8 @@ constexpr int kBwdThreads = 256;
 
 // ------------------------------------------------------------ hc_post bwd ---
 // One workgroup per token.  dx[m] = Σ_n H_res[n,m]·g[n], dy = Σ_n H_post[n]·g[n],
-// dH_res[n,m] = <g[n], x[m]>, dH_post[n] = <g[n], y>, with g = dx_next.
+// dH_res[n,m] = <g[n], x[m]>, dH_post[n] = <g[n], y>, with g = dx_next; the
+// N² + N sums in a fixed order.
 template <int N, int IO>
 __global__ __launch_bounds__(kBwdThreads) void hc_post_bwd_generic(
     const void* __restrict__ dxn, const void* __restrict__ x, const void* __restrict__ y,
@@ -71,12 +72,21 @@ __global__ __launch_bounds__(kBwdThreads) void hc_post_bwd_generic(
       }
     }
   }
-  block_sum<R>(acc, red);
-  if (threadIdx.x == 0) {
+  if constexpr (R <= kWave) {
+    // DPP wave totals and one LDS exchange; lane i of wave 0 writes total i
+    const float tot = wg_sum<R>(acc, red);
+    if (threadIdx.x < N * N)
+      dH_res[t * N * N + threadIdx.x] = tot;
+    else if (threadIdx.x < R)
+      dH_post[t * N + threadIdx.x - N * N] = tot;
+  } else {
+    block_sum<R>(acc, red);
+    if (threadIdx.x == 0) {
 #pragma unroll
-    for (int i = 0; i < N * N; ++i) dH_res[t * N * N + i] = acc[i];
+      for (int i = 0; i < N * N; ++i) dH_res[t * N * N + i] = acc[i];
 #pragma unroll
-    for (int n = 0; n < N; ++n) dH_post[t * N + n] = acc[N * N + n];
+      for (int n = 0; n < N; ++n) dH_post[t * N + n] = acc[N * N + n];
+    }
   }
 }
 

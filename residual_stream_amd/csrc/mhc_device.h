@@ -104,6 +104,55 @@ __device__ __forceinline__ void block_sum(float (&v)[n], float* red) {
   __syncthreads();
 }
 
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_f(float v) {
+  // rows outside ROWS read 0
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xF, true));
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+// Total of v over the 64 lanes of a wave, left in lane 63: sums over 2, 4, 8
+// and 16 lanes by DPP (quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror, row_mirror: each lane adds its partner's partial sum), then
+// row_bcast:15 into rows 1 and 3 and row_bcast:31 into rows 2 and 3, so lane 63
+// holds (r3 + r2) + (r1 + r0).  No LDS round trip, so the sums of many values
+// pipeline.
+__device__ __forceinline__ float wave_total63(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  v += dpp_f<0x142, 0xA>(v);
+  v += dpp_f<0x143, 0xC>(v);
+  return v;
+}
+
+// Sum of R ≤ 64 per-thread values over the workgroup in a fixed order (each
+// wave's total, then the waves in index order).  Returns the totals spread
+// over the lanes: lane i of every wave holds total i (i < R).  `red` holds
+// (blockDim.x / 64)·R floats.  One barrier; a caller that reduces again into
+// the same buffer alternates between two buffers, so that no wave can
+// overwrite partial sums another wave has not read yet.
+template <int R>
+__device__ __forceinline__ float wg_sum(const float (&v)[R], float* red) {
+  static_assert(R <= kWave, "one value per lane");
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  float mine = 0.f;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const float t = lane_f(wave_total63(v[i]), kWave - 1);
+    mine = lane == i ? t : mine;
+  }
+  if (lane < R) red[wave * R + lane] = mine;
+  __syncthreads();
+  float s = 0.f;
+  if (lane < R)
+    for (int w = 0; w < nw; ++w) s += red[w * R + lane];
+  return s;
+}
+
 __device__ __forceinline__ float sigmoid(float z) { return 1.0f / (1.0f + expf(-z)); }
 
 // Calls f(std::integral_constant<int, N>) for the supported stream counts.
