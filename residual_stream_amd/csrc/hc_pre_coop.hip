@@ -171,6 +171,10 @@ __device__ __forceinline__ void coop_body(
   __shared__ __align__(16) uint4 phis[kW][kN][2][64];  // φ B fragments of each compute wave
   __shared__ int ticket_s;
   __shared__ __align__(16) float hq_s[FUSED ? 2 : 1][kTM][kHq];  // incoming coefficients, by tile parity
+  // collapsed h of a tile, by period parity (plain hc_pre): written by the
+  // compute waves in fragment order, stored to HBM the next period as 640-byte
+  // runs per token (a wave's fragment covers only 64 bytes of a token row)
+  __shared__ __align__(16) uint4 hst[FUSED ? 1 : 2][kTM][kW * 4];
 
   // Every call draws exactly gridDim.x tickets, so any run of gridDim.x
   // consecutive counter values covers each residue once: the counter needs
@@ -277,15 +281,23 @@ __device__ __forceinline__ void coop_body(
   const uint4(*bf)[2][64] = phis[wave];
 
 
+    // h of the tile collapsed in period q, from LDS to HBM: thread i stores
+    // piece i (token i / 4kW, 8-d chunk i mod 4kW of the slice)
+    auto flush_h = [&](int64_t q) {
+      static_assert(kTM * kW * 4 == kW * kWave, "one h piece per compute thread");
+      const int64_t rows = rows_of(q - kLag);
+      uint16_t* base = h + (rows > 0 ? tile_of(q - kLag) * kTM * D : 0);
+      const __amdgpu_buffer_rsrc_t hr = make_rsrc(base, (uint32_t)(rows * D * 2));
+      const int tk = threadIdx.x / (kW * 4), c = threadIdx.x % (kW * 4);
+      st16(hr, (uint32_t)((tk * D + slice * kSliceD + 8 * c) * 2), hst[q & 1][tk][c]);
+    };
     auto period = [&](int64_t p, auto j_c) {
       constexpr int J = decltype(j_c)::value;  // p mod kSlots
       constexpr int SP = J;                    // slot of tile p
       constexpr int SC = (J + kAhead) % kSlots;  // slot of tile p − kLag (then of p + kAhead)
+      flush_h(p - 1);  // its LDS buffer is complete: the last period ended with a barrier
       // collapse tile p − kLag
       {
-        const int64_t rows = rows_of(p - kLag);
-        uint16_t* base = h + (rows > 0 ? tile_of(p - kLag) * kTM * D : 0);
-        const __amdgpu_buffer_rsrc_t hr = make_rsrc(base, (uint32_t)(rows * D * 2));
         const float4 hw = *reinterpret_cast<const float4*>(&hpre_s[(p - kLag) & 1][row][0]);
         const float hv[kN] = {hw.x, hw.y, hw.z, hw.w};
         float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -302,9 +314,8 @@ __device__ __forceinline__ void coop_body(
           o[6] += hv[n] * bf16_lo(a.w);
           o[7] += hv[n] * bf16_hi(a.w);
         }
-        st16(hr, (uint32_t)((row * D + d0 + 8 * g) * 2),
-             make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
-                        pack_bf16x2(o[6], o[7])));
+        hst[p & 1][row][wave * 4 + g] = make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                                                   pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7]));
       }
       // loads of tile p + kAhead into the slot just freed
       load_tile(p + kAhead, std::integral_constant<int, SC>{});
@@ -347,6 +358,7 @@ __device__ __forceinline__ void coop_body(
       period(p + 5, std::integral_constant<int, 5>{});
       period(p + 6, std::integral_constant<int, 6>{});
     }
+    flush_h(nper - 1);  // the last period ended with a barrier
    } else {
     // ============ compute waves, fused with the previous hc_post ============
   // Ring of kLag registers sets holding x_next of the tiles waiting for their
