@@ -31,6 +31,10 @@ w only scales the normalised state before the projection, so it is folded
 into the projection's rows, φ' = diag(w)·φ, a [N·D, N²+2N] parameter product
 computed once per step; the per-token work stays in the kernels.
 
+`MHCStack` chains blocks so that each block's write-back and the next block's
+read run as one fused call (`mhc_post_pre`, the pages' inference fusion),
+with the same results as the blocks run one after another.
+
 Every per-token step runs in the library's kernels; this module only wires
 them into autograd.  It needs a GPU and the built library, like the binding.
 """
@@ -167,3 +171,99 @@ class MHCBlock(torch.nn.Module):
         x_next = _Post.apply(x, y.contiguous(), Hq, Hr, self.y_weight, self.out_weight, self.eps,
                              handoff)
         return x_next.reshape(shape)
+
+
+class _PostPre(torch.autograd.Function):
+    """hc_post of block l fused with hc_pre of block l + 1 (`mhc_post_pre`).
+
+    Backward, in the order the separate blocks run it: hc_pre's backward of
+    block l + 1 adds into the hc_post gradient of x_{l+1} that the next
+    boundary handed over, then hc_post's backward of block l; its dx goes to
+    the previous boundary (or block 0's hc_pre) through ``handoff_out``.
+    """
+
+    @staticmethod
+    def forward(ctx, x, y, H_post_in, H_res_in, phi, bias, alpha, iters, eps, handoff_in, handoff_out):
+        alphas = tuple(float(a) for a in alpha.tolist())
+        x_next, h, Hp, Hq, Hr = mhc.mhc_post_pre(x, y, H_post_in, H_res_in, phi, bias, iters=iters,
+                                                 eps=eps, alphas=alphas)
+        ctx.save_for_backward(x, y, H_post_in, H_res_in, x_next, phi, bias)
+        ctx.cfg = (iters, eps, alphas, alpha.requires_grad)
+        ctx.handoff_in, ctx.handoff_out = handoff_in, handoff_out
+        ctx.mark_non_differentiable(Hp)
+        return x_next, h, Hp, Hq, Hr
+
+    @staticmethod
+    def backward(ctx, dxn, dh, _dHp, dHq, dHr):
+        x, y, H_post_in, H_res_in, x_next, phi, bias = ctx.saved_tensors
+        iters, eps, alphas, want_dalpha = ctx.cfg
+        T, N, D = x.shape
+        dx_next = ctx.handoff_in.dx
+        ctx.handoff_in.dx = None
+        if dx_next is None:
+            dx_next = torch.zeros_like(x_next)
+        if dxn is not None:  # x_{l+1} also used outside the stack
+            dx_next = dx_next + dxn
+        if dh is None:
+            dh = torch.zeros((T, D), dtype=x.dtype, device=x.device)
+        if dHq is None:
+            dHq = torch.zeros((T, N), dtype=torch.float32, device=x.device)
+        if dHr is None:
+            dHr = torch.zeros((T, N, N), dtype=torch.float32, device=x.device)
+        dx_next, dphi, dbias, dalpha = mhc.mhc_pre_bwd(
+            dh.contiguous(), x_next, phi, bias, dHq.contiguous(), dHr.contiguous(), dx_next,
+            iters=iters, eps=eps, alphas=alphas, want_dalpha=want_dalpha)
+        dx, dy, dHq_in, dHr_in = mhc.mhc_post_bwd(dx_next, x, y, H_post_in, H_res_in)
+        ctx.handoff_out.dx = dx
+        dalpha = dalpha.cpu() if want_dalpha else None
+        return None, dy, dHq_in, dHr_in, dphi, dbias, dalpha, None, None, None, None
+
+
+class MHCStack(torch.nn.Module):
+    """Consecutive `MHCBlock`s run with each block's write-back fused to the
+    next block's read (openPangu 2.0 analysis §11.3; `mhc_post_pre`): the state
+    between two blocks is written once and not read back.
+
+    Uses the blocks' own parameters and sublayers, so a stack and the same
+    blocks applied one after another compute the same values (bit for bit:
+    the fused forward equals hc_post followed by hc_pre, and the backward runs
+    the same kernels in the same order).  For the plain write-back only: a
+    block with a sandwich or post-norm, or with recompute, is rejected.
+    """
+
+    def __init__(self, blocks):
+        super().__init__()
+        self.blocks = torch.nn.ModuleList(blocks)
+        if not len(self.blocks):
+            raise ValueError("MHCStack needs at least one block")
+        b0 = self.blocks[0]
+        for b in self.blocks:
+            if b.y_weight is not None or b.out_weight is not None:
+                raise ValueError("MHCStack fuses the plain write-back only (no sandwich or post-norm)")
+            if b.recompute:
+                raise ValueError("MHCStack does not checkpoint sublayers")
+            if (b.N, b.D, b.iters, b.eps) != (b0.N, b0.D, b0.iters, b0.eps):
+                raise ValueError("all blocks of a stack need the same N, D, rounds and eps")
+
+    def forward(self, x):
+        blocks = self.blocks
+        b0 = blocks[0]
+        shape = x.shape
+        if x.dim() == 4:
+            x = x.reshape(-1, shape[-2], shape[-1])
+        if x.shape[1:] != (b0.N, b0.D):
+            raise ValueError(f"expected [..., {b0.N}, {b0.D}] state, got {tuple(shape)}")
+        x = x.contiguous()
+        handoff = _DxHandoff()
+        h, _Hp, Hq, Hr = _Pre.apply(x, b0._phi(), b0.bias, b0.alpha, b0.iters, b0.eps, handoff)
+        for i, b in enumerate(blocks):
+            y = b.sublayer(h).contiguous()
+            if i + 1 < len(blocks):
+                nb = blocks[i + 1]
+                nxt = _DxHandoff()
+                x, h, _Hp, Hq, Hr = _PostPre.apply(x, y, Hq, Hr, nb._phi(), nb.bias, nb.alpha, nb.iters,
+                                                   nb.eps, nxt, handoff)
+                handoff = nxt
+            else:
+                x = _Post.apply(x, y, Hq, Hr, None, None, b.eps, handoff)
+        return x.reshape(shape)

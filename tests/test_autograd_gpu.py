@@ -146,3 +146,57 @@ def test_stabilised_block_matches_oracle(io, T, D):
     assert_close("dy_weight", host(block.y_weight.grad), post["dy_weight"], tol)
     assert_close("dout_weight", host(block.out_weight.grad), post["dout_weight"], tol)
     assert_close("dpre_weight", host(block.pre_weight.grad), pb["dnorm_weight"], tol)
+
+
+@pytest.mark.parametrize("io,D,L", [("bf16", 2560, 3), ("bf16", 5120, 2), ("f32", 256, 3)])
+def test_stack_equals_blocks_one_after_another(io, D, L):
+    # the fused boundary (mhc_post_pre) equals hc_post then hc_pre bit for bit,
+    # and the stack's backward runs the blocks' kernels in the same order:
+    # outputs and every gradient must be identical (bf16 at D = 2560 / 5120 runs
+    # the fused split-K kernel; the f32 case its two-kernel fallback)
+    _say(f"[autograd] stack of {L} blocks vs blocks in sequence, io={io} D={D}")
+    from residual_stream_amd.autograd import MHCBlock, MHCStack
+
+    N, T = 4, 70
+    blocks = []
+    for li in range(L):
+        inp_l = make_inputs(T, N, D, io=io, seed=50 + li, alpha=0.3)
+        c = make_norm_weights(N, D, seed=60 + li)[0]
+        b = MHCBlock(_Scale(dev(c, io)), N, D, iters=inp_l.iters, eps=inp_l.eps, alpha=inp_l.alphas,
+                     train_alpha=True)
+        with torch.no_grad():
+            b.phi.copy_(dev(inp_l.phi))
+            b.bias.copy_(dev(inp_l.bias))
+        blocks.append(b)
+    inp = make_inputs(T, N, D, io=io, seed=49, grads=True)
+    g = dev(inp.dx_next, io).float()
+    params = [p for b in blocks for p in (b.phi, b.bias, b.alpha)]
+
+    def run(fn):
+        for p in params:
+            p.grad = None
+        x = dev(inp.x, io).requires_grad_(True)
+        out = fn(x)
+        (out.float() * g).sum().backward()
+        torch.cuda.synchronize()
+        return out.detach(), x.grad, [p.grad.clone() for p in params]
+
+    def chain(x):
+        for b in blocks:
+            x = b(x)
+        return x
+
+    a = run(chain)
+    s = run(MHCStack(blocks))
+    assert torch.equal(a[0], s[0]), "x_L differs"
+    assert torch.equal(a[1], s[1]), "dx differs"
+    for i, (u, v) in enumerate(zip(a[2], s[2])):
+        assert torch.equal(u, v), f"parameter gradient {i} differs"
+
+
+def test_stack_rejects_stabilised_blocks():
+    from residual_stream_amd.autograd import MHCBlock, MHCStack
+
+    b = MHCBlock(torch.nn.Identity(), 4, 64, sandwich_norm=True)
+    with pytest.raises(ValueError):
+        MHCStack([b, MHCBlock(torch.nn.Identity(), 4, 64)])
