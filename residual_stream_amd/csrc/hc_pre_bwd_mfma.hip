@@ -1,4 +1,5 @@
-// hc_pre backward on the matrix cores (bf16 I/O, N = 4, D a multiple of 256).
+// hc_pre backward, tiled (N = 4, D a multiple of 256): the matrix cores for
+// bf16 I/O, the fp32 vector ALUs for fp32 I/O.
 //
 // Exact derivative of the openPangu 2.0 analysis §5.3 formula block, with the
 // forward recomputed from x (Ascend mHC Triton article, intra-layer recompute
@@ -679,6 +680,317 @@ __global__ __launch_bounds__(kDxThreads, 2) void bwd_dx_kernel(
   }
 }
 
+// ------------------------------------------------- fp32 I/O, passes 1 and 3 ---
+// The same three passes for fp32 x, dh and dx, on the fp32 vector ALUs (the
+// matrix cores' bf16 inputs would not keep fp32 accuracy).  Both kernels own a
+// slice of 128 d (all four streams: 512 k) and walk a token range in tiles of
+// 16 tokens, with φ's slice in LDS for the whole range, so φ is read once per
+// workgroup instead of once per token.  Global traffic is linear (thread i
+// moves the float4 pieces i, i + 256, … of a tile: 512-byte runs of every
+// token row); products run from LDS with register blocking (eight or more
+// fused multiply-adds per LDS read).  They write the records and the dφ
+// partials of the bf16 path's layout, so its coefficient and sum kernels
+// finish the job.
+constexpr int kFD = 128;               // d per slice
+constexpr int kFK = kN * kFD;          // k per slice
+constexpr int kFT = 16;                // tokens per tile
+constexpr int kFThreads = 256;
+constexpr int kFRow = kFK + 4;         // floats per token row of an x / dx̄ tile in LDS
+constexpr int kFHRow = kFD + 4;        // floats per token row of a dh tile
+constexpr int kFX4 = kFT * kFK / 4 / kFThreads;  // x float4 pieces per thread per tile (8)
+constexpr int kFH4 = kFT * kFD / 4 / kFThreads;  // dh float4 pieces per thread per tile (2)
+static_assert(kFX4 == 8 && kFH4 == 2, "tile pieces");
+
+__device__ __forceinline__ float4 ldf4(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  const uint4 v = ld16(r, voff);
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+}
+
+// Tile pieces of thread `tid`: x piece q = tid + 256j is token q / 128,
+// stream (q / 32) mod 4, d4 = q mod 32 (d = 4·d4 within the slice); dh piece
+// q = tid + 256j is token q / 32, d4 = q mod 32.
+struct FPieces {
+  uint32_t gx[kFX4], gh[kFH4];  // byte offsets within the tile's rows in HBM
+  int lx[kFX4], lh[kFH4];       // float offsets in the LDS tiles
+  __device__ FPieces(int tid, int D, int slice) {
+    const int K = kN * D;
+#pragma unroll
+    for (int j = 0; j < kFX4; ++j) {
+      const int q = tid + kFThreads * j, tk = q / 128, n = (q / 32) % kN, d4 = q % 32;
+      gx[j] = (uint32_t)((tk * K + n * D + slice * kFD + 4 * d4) * 4);
+      lx[j] = tk * kFRow + n * kFD + 4 * d4;
+    }
+#pragma unroll
+    for (int j = 0; j < kFH4; ++j) {
+      const int q = tid + kFThreads * j, tk = q / 32, d4 = q % 32;
+      gh[j] = (uint32_t)((tk * D + slice * kFD + 4 * d4) * 4);
+      lh[j] = tk * kFHRow + 4 * d4;
+    }
+  }
+};
+
+// Pass 1, fp32.  Grid (D / 128 slices, token splits of R tokens).  Record of
+// each (slice, token): p[24] = x·φ over the slice, ss = Σ x², dhp[n] = Σ_d
+// dh·x[n] (the layout of the bf16 pass).
+__global__ __launch_bounds__(kFThreads, 1) void bwd_proj_f32_kernel(
+    const float* __restrict__ x, const float* __restrict__ dh, const float* __restrict__ phi,
+    float* __restrict__ part, int64_t T, int D, int64_t R) {
+  __shared__ __align__(16) float phs[kFK * kC];         // φ[k][c] of the slice
+  __shared__ __align__(16) float xs[kFT * kFRow];       // x[t][k] of the tile
+  __shared__ __align__(16) float hsh[kFT * kFHRow];     // dh[t][d]
+  __shared__ __align__(16) float red[16][kFT][kC];      // products by k-split
+  const int slice = blockIdx.x, tid = threadIdx.x;
+  const int64_t tb = (int64_t)blockIdx.y * R;
+  const int64_t te = tb + R < T ? tb + R : T;
+  const int nblk = te > tb ? (int)((te - tb + kFT - 1) / kFT) : 0;
+  const int K = kN * D;
+  const FPieces pc(tid, D, slice);
+  // φ slice: rows n·D + slice·128 + dd of every stream, contiguous per stream
+  for (int i = tid; i < kFK * kC / 4; i += kFThreads) {
+    const int kl = i / (kC / 4), c4 = i % (kC / 4), n = kl / kFD, dd = kl % kFD;
+    reinterpret_cast<float4*>(phs)[i] =
+        reinterpret_cast<const float4*>(phi + ((int64_t)n * D + slice * kFD + dd) * kC)[c4];
+  }
+  float4 rx[kFX4], rh[kFH4];
+  auto load = [&](int b) {
+    const int64_t t0 = tb + (int64_t)kFT * b;
+    const int64_t rows = b < nblk ? (te - t0 < kFT ? te - t0 : kFT) : 0;
+    const int64_t base = rows > 0 ? t0 : 0;
+    const auto ax = make_rsrc(x + base * K, (uint32_t)(rows * K * 4));
+    const auto ah = make_rsrc(dh + base * D, (uint32_t)(rows * D * 4));
+#pragma unroll
+    for (int j = 0; j < kFX4; ++j) rx[j] = ldf4(ax, pc.gx[j]);
+#pragma unroll
+    for (int j = 0; j < kFH4; ++j) rh[j] = ldf4(ah, pc.gh[j]);
+  };
+  // product roles: k-split ks (32 k), tokens 4·tb4 .. +3, columns 6·cb .. +5
+  const int ks = tid / 16, tb4 = (tid / 4) % 4, cb = tid % 4;
+  // sum roles: token st, stream sn, quarter sq (32 d)
+  const int st = tid / 16, sn = (tid / 4) % 4, sq = tid % 4;
+  load(0);
+  for (int b = 0; b < nblk; ++b) {
+#pragma unroll
+    for (int j = 0; j < kFX4; ++j) *reinterpret_cast<float4*>(xs + pc.lx[j]) = rx[j];
+#pragma unroll
+    for (int j = 0; j < kFH4; ++j) *reinterpret_cast<float4*>(hsh + pc.lh[j]) = rh[j];
+    __syncthreads();
+    load(b + 1);  // the next tile streams while this one is worked on
+    float acc[4][6];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 6; ++c) acc[a][c] = 0.f;
+    for (int kk = 0; kk < 32; kk += 4) {
+      const int k = ks * 32 + kk;
+      float4 xv[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) xv[a] = *reinterpret_cast<const float4*>(xs + (4 * tb4 + a) * kFRow + k);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float2* pr = reinterpret_cast<const float2*>(phs + (k + e) * kC + 6 * cb);
+        const float2 f0 = pr[0], f1 = pr[1], f2 = pr[2];
+        const float ph[6] = {f0.x, f0.y, f1.x, f1.y, f2.x, f2.y};
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const float xe = e == 0 ? xv[a].x : (e == 1 ? xv[a].y : (e == 2 ? xv[a].z : xv[a].w));
+#pragma unroll
+          for (int c = 0; c < 6; ++c) acc[a][c] = __builtin_fmaf(xe, ph[c], acc[a][c]);
+        }
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 6; ++c) red[ks][4 * tb4 + a][6 * cb + c] = acc[a][c];
+    // Σ x² and <dh, x[n]> of token st over quarter sq of stream sn
+    float ssp = 0.f, dpp = 0.f;
+#pragma unroll 8
+    for (int dd = 0; dd < 32; ++dd) {
+      const float xv = xs[st * kFRow + sn * kFD + sq * 32 + dd];
+      ssp = __builtin_fmaf(xv, xv, ssp);
+      dpp = __builtin_fmaf(hsh[st * kFHRow + sq * 32 + dd], xv, dpp);
+    }
+    // lanes 16·st .. 16·st + 15 hold (sn, sq): quads sum the quarters, the
+    // row sums the streams (fixed order)
+    dpp = dpp_f<0x4E>(dpp) + dpp;  // sq ^ 2
+    dpp = dpp_f<0xB1>(dpp) + dpp;  // sq ^ 1
+    ssp = dpp_f<0x4E>(ssp) + ssp;
+    ssp = dpp_f<0xB1>(ssp) + ssp;
+    ssp = dpp_f<0x141>(ssp) + ssp;
+    ssp = dpp_f<0x140>(ssp) + ssp;
+    __syncthreads();
+    const int64_t t0 = tb + (int64_t)kFT * b;
+    for (int o = tid; o < kFT * kC; o += kFThreads) {
+      const int tk = o / kC, c = o % kC;
+      float v = 0.f;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) v += red[q][tk][c];
+      if (t0 + tk < te) part[((int64_t)slice * T + t0 + tk) * kPartStride + c] = v;
+    }
+    if (sq == 0 && t0 + st < te) {
+      float* rec = part + ((int64_t)slice * T + t0 + st) * kPartStride;
+      rec[kC + 1 + sn] = dpp;
+      if (sn == 0) rec[kC] = ssp;
+    }
+    __syncthreads();  // the tiles and red are rewritten next
+  }
+}
+
+// Pass 3, fp32.  Grid (D / 128 slices, TS token splits of tps tokens).  Per
+// tile: dx̄ = G·φᵀ into LDS; dφ += xᵀ·G kept in registers for the whole
+// range; then dx += dx̄ − β·x + H_pre[n]·dh piece by piece.  The workgroup's dφ
+// partial rows go to dphi_part[split][k][c].
+__global__ __launch_bounds__(kFThreads, 1) void bwd_dx_f32_kernel(
+    const float* __restrict__ x, const float* __restrict__ dh, const float* __restrict__ phi,
+    const float* __restrict__ coef, float* __restrict__ dx, float* __restrict__ dphi_part, int64_t T,
+    int D, int64_t tps) {
+  __shared__ __align__(16) float pht[kC * kFK];        // φ[k][c] of the slice, transposed: [c][k]
+  __shared__ __align__(16) float xs[kFT * kFRow];      // x[t][k]
+  __shared__ __align__(16) float dxr[kFT * kFRow];     // (G·φᵀ)[t][k]
+  __shared__ __align__(16) float hsh[kFT * kFHRow];    // dh[t][d]
+  __shared__ __align__(16) float gct[kC * kFT];        // G[c][t]
+  __shared__ __align__(16) float gtc[kFT * kC];        // G[t][c]
+  __shared__ float bs[kFT];                            // β
+  __shared__ __align__(16) float hps[kFT][kN];         // H_pre
+  const int slice = blockIdx.x, split = blockIdx.y, tid = threadIdx.x;
+  const int64_t tb = (int64_t)split * tps;
+  const int64_t te = tb + tps < T ? tb + tps : T;
+  const int nblk = te > tb ? (int)((te - tb + kFT - 1) / kFT) : 0;
+  const int K = kN * D;
+  const FPieces pc(tid, D, slice);
+  for (int i = tid; i < kFK * kC; i += kFThreads) {
+    const int kl = i / kC, c = i % kC, n = kl / kFD, dd = kl % kFD;
+    pht[c * kFK + kl] = phi[((int64_t)n * D + slice * kFD + dd) * kC + c];
+  }
+  float4 rx[kFX4], rh[kFH4], rd[kFX4];
+  float4 rc;  // coefficients: threads < 160 hold float4 (tid mod 10) of token tid / 10
+  auto load = [&](int b) {
+    const int64_t t0 = tb + (int64_t)kFT * b;
+    const int64_t rows = b < nblk ? (te - t0 < kFT ? te - t0 : kFT) : 0;
+    const int64_t base = rows > 0 ? t0 : 0;
+    const auto ax = make_rsrc(x + base * K, (uint32_t)(rows * K * 4));
+    const auto ad = make_rsrc(dx + base * K, (uint32_t)(rows * K * 4));
+    const auto ah = make_rsrc(dh + base * D, (uint32_t)(rows * D * 4));
+    const auto ac = make_rsrc(coef + base * kCoefStride, (uint32_t)(rows * kCoefStride * 4));
+#pragma unroll
+    for (int j = 0; j < kFX4; ++j) rx[j] = ldf4(ax, pc.gx[j]);
+#pragma unroll
+    for (int j = 0; j < kFX4; ++j) rd[j] = ldf4(ad, pc.gx[j]);
+#pragma unroll
+    for (int j = 0; j < kFH4; ++j) rh[j] = ldf4(ah, pc.gh[j]);
+    // token tid / 10, floats 4·(tid mod 10) .. +3 of its 40 (G[24], pad, β at 32, H_pre 33..36)
+    rc = ldf4(ac, tid < kFT * 10 ? (uint32_t)(((tid / 10) * kCoefStride + 4 * (tid % 10)) * 4) : 0x7FFFFFF0u);
+  };
+  // dx̄ roles: tokens 4·db .. +3, k 8·dk .. +7
+  const int db = tid / 64, dk = tid % 64;
+  // dφ roles: k 8·fk .. +7, columns 6·fc .. +5
+  const int fk = tid / 4, fc = tid % 4;
+  float dph[8][6];
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+#pragma unroll
+    for (int c = 0; c < 6; ++c) dph[e][c] = 0.f;
+  load(0);
+  for (int b = 0; b < nblk; ++b) {
+    const int64_t t0 = tb + (int64_t)kFT * b;
+#pragma unroll
+    for (int j = 0; j < kFX4; ++j) *reinterpret_cast<float4*>(xs + pc.lx[j]) = rx[j];
+#pragma unroll
+    for (int j = 0; j < kFH4; ++j) *reinterpret_cast<float4*>(hsh + pc.lh[j]) = rh[j];
+    float4 dxin[kFX4];
+#pragma unroll
+    for (int j = 0; j < kFX4; ++j) dxin[j] = rd[j];
+    if (tid < kFT * 10) {
+      const int tk = tid / 10, q = tid % 10;
+      const float v[4] = {rc.x, rc.y, rc.z, rc.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int f = 4 * q + e;
+        if (f < kC) {
+          gct[f * kFT + tk] = v[e];
+          gtc[tk * kC + f] = v[e];
+        } else if (f == 32) {
+          bs[tk] = v[e];
+        } else if (f >= 33 && f < 33 + kN) {
+          hps[tk][f - 33] = v[e];
+        }
+      }
+    }
+    __syncthreads();
+    load(b + 1);
+    // dx̄ = G·φᵀ for 4 tokens × 8 k
+    {
+      float acc[4][8];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[a][e] = 0.f;
+#pragma unroll 4
+      for (int c = 0; c < kC; ++c) {
+        const float4 g = *reinterpret_cast<const float4*>(gct + c * kFT + 4 * db);
+        const float4 p0 = *reinterpret_cast<const float4*>(pht + c * kFK + 8 * dk);
+        const float4 p1 = *reinterpret_cast<const float4*>(pht + c * kFK + 8 * dk + 4);
+        const float gv[4] = {g.x, g.y, g.z, g.w};
+        const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[a][e] = __builtin_fmaf(gv[a], pv[e], acc[a][e]);
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        float* r = dxr + (4 * db + a) * kFRow + 8 * dk;
+        *reinterpret_cast<float4*>(r) = make_float4(acc[a][0], acc[a][1], acc[a][2], acc[a][3]);
+        *reinterpret_cast<float4*>(r + 4) = make_float4(acc[a][4], acc[a][5], acc[a][6], acc[a][7]);
+      }
+    }
+    // dφ += xᵀ·G over the tile's tokens (tokens past the range have x = 0, G = 0)
+#pragma unroll 4
+    for (int tk = 0; tk < kFT; ++tk) {
+      const float4 x0 = *reinterpret_cast<const float4*>(xs + tk * kFRow + 8 * fk);
+      const float4 x1 = *reinterpret_cast<const float4*>(xs + tk * kFRow + 8 * fk + 4);
+      const float2* gp = reinterpret_cast<const float2*>(gtc + tk * kC + 6 * fc);
+      const float2 g0 = gp[0], g1 = gp[1], g2 = gp[2];
+      const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      const float gv[6] = {g0.x, g0.y, g1.x, g1.y, g2.x, g2.y};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int c = 0; c < 6; ++c) dph[e][c] = __builtin_fmaf(xv[e], gv[c], dph[e][c]);
+    }
+    __syncthreads();
+    // dx += dx̄ − β·x + H_pre[n]·dh, piece by piece (stores dropped past the range)
+    {
+      const int64_t rows = t0 < te ? (te - t0 < kFT ? te - t0 : kFT) : 0;
+      const auto ad = make_rsrc(dx + (rows > 0 ? t0 : 0) * K, (uint32_t)(rows * K * 4));
+#pragma unroll
+      for (int j = 0; j < kFX4; ++j) {
+        const int q = tid + kFThreads * j, tk = q / 128, n = (q / 32) % kN, d4 = q % 32;
+        const float4 r = *reinterpret_cast<const float4*>(dxr + pc.lx[j]);
+        const float4 xv = *reinterpret_cast<const float4*>(xs + pc.lx[j]);
+        const float4 hv = *reinterpret_cast<const float4*>(hsh + tk * kFHRow + 4 * d4);
+        const float be = bs[tk], hp = hps[tk][n];
+        float4 o = dxin[j];
+        o.x += r.x - be * xv.x + hp * hv.x;
+        o.y += r.y - be * xv.y + hp * hv.y;
+        o.z += r.z - be * xv.z + hp * hv.z;
+        o.w += r.w - be * xv.w + hp * hv.w;
+        st16(ad, pc.gx[j], make_uint4(__float_as_uint(o.x), __float_as_uint(o.y), __float_as_uint(o.z),
+                                      __float_as_uint(o.w)));
+      }
+    }
+    __syncthreads();  // the tiles are rewritten next
+  }
+  // this split's dφ rows of the slice
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int kl = 8 * fk + e, n = kl / kFD, dd = kl % kFD;
+    float* row = dphi_part + ((int64_t)split * K + (int64_t)n * D + slice * kFD + dd) * kC + 6 * fc;
+#pragma unroll
+    for (int c = 0; c < 6; ++c) row[c] = dph[e][c];
+  }
+}
+
 // dφ = Σ_s part[s] in split order.  Workgroup 0 sums the dbias / dα rows
 // instead (one row per 16 tokens), in a fixed order.
 __global__ __launch_bounds__(256) void dphi_bias_sum_kernel(const float* __restrict__ part,
@@ -758,9 +1070,10 @@ static Layout layout(const mhc_desc& d) {
   Layout L;
   const size_t T = (size_t)d.T, K = (size_t)kN * d.D;
   // projection slices of 320 d (ten waves) when D allows, else 256 d (eight);
-  // about one workgroup per CU of a 256-CU chip, whole 16-token blocks
+  // fp32: slices of 128 d.  About one workgroup per CU of a 256-CU chip,
+  // whole 16-token blocks
   L.W = d.D % 320 == 0 ? 10 : 8;
-  L.S = d.D / (32 * L.W);
+  L.S = d.io == kF32 ? d.D / kFD : d.D / (32 * L.W);
   const int64_t blocks = (d.T + 15) / 16;
   int64_t ps = 256 / L.S;
   if (ps > blocks) ps = blocks;
@@ -771,7 +1084,8 @@ static Layout layout(const mhc_desc& d) {
   // 256-CU chip (K/512 slices × TS ≤ 512, two resident per CU), at most one
   // split per 16-token tile
   const int64_t nsl = (int64_t)K / kDxK;
-  int64_t ts = 512 / nsl;
+  // (the fp32 kernel holds one workgroup per CU: one round of them)
+  int64_t ts = (d.io == kF32 ? 256 : 512) / nsl;
   const int64_t tiles = (d.T + kDxTile - 1) / kDxTile;
   if (ts > tiles) ts = tiles;
   L.TS = (int)(ts < 1 ? 1 : (ts > 32 ? 32 : ts));
@@ -787,7 +1101,7 @@ static Layout layout(const mhc_desc& d) {
 }  // namespace bwdm
 
 bool pre_bwd_mfma_eligible(const mhc_desc& d) {
-  return d.N == 4 && d.io == kBF16 && d.D % bwdm::kSliceD == 0 && d.sinkhorn_iters <= 64;
+  return d.N == 4 && (d.io == kBF16 || d.io == kF32) && d.D % bwdm::kSliceD == 0 && d.sinkhorn_iters <= 64;
 }
 
 size_t pre_bwd_mfma_workspace_bytes(const mhc_desc& d) { return bwdm::layout(d).total; }
@@ -807,7 +1121,10 @@ hipError_t launch_pre_bwd_mfma(const mhc_desc& d, const void* dh, const void* x,
   const int64_t T = d.T;
   const int K = kN * d.D;
   const dim3 pgrid((unsigned)L.S, (unsigned)L.PS);
-  if (L.W == 10)
+  if (d.io == kF32)
+    hipLaunchKernelGGL(bwd_proj_f32_kernel, pgrid, dim3(kFThreads), 0, s, static_cast<const float*>(x),
+                       static_cast<const float*>(dh), phi, part, T, d.D, L.R);
+  else if (L.W == 10)
     hipLaunchKernelGGL(bwd_proj_kernel<10>, pgrid, dim3(640), 0, s, static_cast<const uint16_t*>(x),
                        static_cast<const uint16_t*>(dh), phi, part, T, d.D, L.R);
   else
@@ -821,9 +1138,14 @@ hipError_t launch_pre_bwd_mfma(const mhc_desc& d, const void* dh, const void* x,
                      d.eps, d.alpha_pre, d.alpha_post, d.alpha_res);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t tps = ((T + L.TS - 1) / L.TS + kDxTile - 1) / kDxTile * kDxTile;  // tokens per split
-  hipLaunchKernelGGL(bwd_dx_kernel, dim3((unsigned)(K / kDxK), (unsigned)L.TS), dim3(kDxThreads), 0, s,
-                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dh), phi, coef,
-                     static_cast<uint16_t*>(dx), dphi_part, T, d.D, tps);
+  if (d.io == kF32)
+    hipLaunchKernelGGL(bwd_dx_f32_kernel, dim3((unsigned)(d.D / kFD), (unsigned)L.TS), dim3(kFThreads), 0, s,
+                       static_cast<const float*>(x), static_cast<const float*>(dh), phi, coef,
+                       static_cast<float*>(dx), dphi_part, T, d.D, tps);
+  else
+    hipLaunchKernelGGL(bwd_dx_kernel, dim3((unsigned)(K / kDxK), (unsigned)L.TS), dim3(kDxThreads), 0, s,
+                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dh), phi, coef,
+                       static_cast<uint16_t*>(dx), dphi_part, T, d.D, tps);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t KC = (int64_t)K * kC;
   hipLaunchKernelGGL(dphi_bias_sum_kernel, dim3((unsigned)((KC + 255) / 256 + 1)), dim3(256), 0, s,

@@ -108,13 +108,15 @@ def test_backward_shapes(io, N, T, D):
     check_backward(make_inputs(T, N, D, io=io, seed=100 + T + N + D, alpha=1.0, grads=True))
 
 
+@pytest.mark.parametrize("io", ["bf16", "f32"])
 @pytest.mark.parametrize("D", [256, 512, 2560])
 @pytest.mark.parametrize("T", [1, 5, 70, 300])
 @pytest.mark.parametrize("alpha", [0.01, 1.0])
-def test_backward_matrix_core_shapes(D, T, alpha):
-    # bf16 I/O, N = 4, D a multiple of 256: the split-K / per-slice matrix-core
-    # backward; token counts exercise partial tiles and partial token splits.
-    check_backward(make_inputs(T, 4, D, io="bf16", seed=7 * T + D, alpha=alpha, grads=True))
+def test_backward_matrix_core_shapes(io, D, T, alpha):
+    # N = 4, D a multiple of 256: the tiled backward (matrix cores for bf16,
+    # fp32 vector ALUs for fp32); token counts exercise partial tiles and
+    # partial token splits.
+    check_backward(make_inputs(T, 4, D, io=io, seed=7 * T + D, alpha=alpha, grads=True))
 
 
 @pytest.mark.parametrize("alpha", [0.01, 1.0])
@@ -205,6 +207,14 @@ def _sample_tokens(T, n=40, seed=0):
 def test_full_size_forward_sampled(T, D, io):
     inp = make_inputs(T, 4, D, io=io, seed=0)
     check_forward(inp, tokens=_sample_tokens(T))
+
+
+@pytest.mark.parametrize("T,D", [(1024, 5120), (2048, 2560)])
+def test_full_size_backward_fp32(T, D):
+    # the fp32 workloads (Pro width S=1024, Flash width S=2048): dx, dy, dH_* on
+    # sampled tokens, dφ / dbias / dα against the full fp64 oracle
+    inp = make_inputs(T, 4, D, io="f32", seed=1, grads=True)
+    check_backward(inp, tokens=_sample_tokens(T))
 
 
 def test_full_size_backward_long_sequence_bf16():
