@@ -96,7 +96,10 @@ size_t mhc_pre_workspace_bytes(const mhc_desc* desc);
  * stream they never do).  Those workgroups wait for each other with bounded
  * waits; should one never arrive (e.g. far too few free compute units), the
  * affected tokens get NaN in h and in the coefficients rather than a hang or
- * silently wrong values. */
+ * silently wrong values.  The tag is drawn on the host when the call is made:
+ * a HIP graph that replays a captured split-K call reuses it, so each replay
+ * must find the workspace cleared (zero-filled by a kernel recorded in the same
+ * graph before the call; zero never matches a tag). */
 mhc_status mhc_pre(const mhc_desc* desc, const void* x, const float* phi, const float* bias,
                    void* h, float* H_pre, float* H_post, float* H_res,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);

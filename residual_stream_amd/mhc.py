@@ -151,6 +151,16 @@ def _f32(t: torch.Tensor) -> torch.Tensor:
     return t
 
 
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    """A workspace for one call.  Under stream capture it is zero-filled (a fill
+    kernel, recorded in the graph): the split-K hc_pre tags its exchange
+    records with a number drawn at launch, which a replayed graph repeats, so
+    each replay must start from records that match no tag."""
+    if torch.cuda.is_current_stream_capturing():
+        return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
 def desc_for(x: torch.Tensor, iters: int = 20, eps: float = 1e-6, alphas=(0.01, 0.01, 0.01)):
     T, N, D = x.shape
     return make_desc(T, N, D, _io_of(x), iters, eps, alphas)
@@ -172,7 +182,7 @@ def mhc_pre(x, phi, bias, *, iters=20, eps=1e-6, alphas=(0.01, 0.01, 0.01), out=
     h, Hp, Hq, Hr = out
     need = lib.mhc_pre_workspace_bytes(ctypes.byref(d))
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        workspace = _workspace(need, x.device)
     nbytes = workspace.numel() if workspace is not None else 0
     st = lib.mhc_pre(ctypes.byref(d), _ptr(x), _ptr(_f32(phi)), _ptr(_f32(bias)), _ptr(h), _ptr(Hp),
                      _ptr(Hq), _ptr(Hr), _ptr(workspace), nbytes, _stream(stream))
@@ -227,7 +237,7 @@ def mhc_pre_bwd(dh, x, phi, bias, dH_post, dH_res, dx, *, iters=20, eps=1e-6,
     dphi, dbias, dalpha = out
     need = lib.mhc_pre_bwd_workspace_bytes(ctypes.byref(d))
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        workspace = _workspace(need, x.device)
     nbytes = workspace.numel() if workspace is not None else 0
     st = lib.mhc_pre_bwd(ctypes.byref(d), _ptr(dh), _ptr(x), _ptr(_f32(phi)), _ptr(_f32(bias)),
                          _ptr(_f32(dH_post)), _ptr(_f32(dH_res)), _ptr(dx), _ptr(dphi),
@@ -253,7 +263,7 @@ def mhc_post_pre(x, y, H_post, H_res, phi, bias, *, iters=20, eps=1e-6, alphas=(
     xn, h, Hp, Hq, Hr = out
     need = lib.mhc_post_pre_workspace_bytes(ctypes.byref(d))
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        workspace = _workspace(need, x.device)
     nbytes = workspace.numel() if workspace is not None else 0
     st = lib.mhc_post_pre(ctypes.byref(d), _ptr(x), _ptr(y), _ptr(_f32(H_post)), _ptr(_f32(H_res)),
                           _ptr(_f32(phi)), _ptr(_f32(bias)), _ptr(xn), _ptr(h), _ptr(Hp), _ptr(Hq),
@@ -308,7 +318,7 @@ def mhc_post_stable_bwd(dx_next, x, y, H_post, H_res, *, y_weight=None, out_weig
     dx, dy, dHp, dHr, dyw, dow = out
     need = lib.mhc_post_stable_bwd_workspace_bytes(ctypes.byref(d), int(sw), int(pn))
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        workspace = _workspace(need, x.device)
     nbytes = workspace.numel() if workspace is not None else 0
     st = lib.mhc_post_stable_bwd(
         ctypes.byref(d), _ptr(dx_next), _ptr(x), _ptr(y),

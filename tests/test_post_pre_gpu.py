@@ -103,3 +103,45 @@ def test_fused_rejects_aliasing():
         mhc.mhc_post_pre(x, y, Hq, Hr, dev(b.phi), dev(b.bias),
                          out=(x, torch.empty_like(y), torch.empty_like(Hq), torch.empty_like(Hq),
                               torch.empty_like(Hr)))
+
+
+def test_graph_replay_with_cleared_workspace_matches_eager():
+    # the split-K hc_pre (and the fused call) captured in a graph together with a
+    # zero fill of the workspace; replayed with new input contents, every replay
+    # must equal the eager call on the same inputs, bit for bit
+    _say("[graph] split-K hc_pre and mhc_post_pre under graph replay")
+    T, N, D = 300, 4, 5120
+    sets = [make_inputs(T, N, D, io="bf16", seed=s, alpha=0.3) for s in (31, 32, 33)]
+    Hq0, Hr0 = make_coefficients(T, N, seed=34)
+    Hq0, Hr0 = dev(Hq0), dev(Hr0)
+    x = dev(sets[0].x, "bf16")
+    y = dev(sets[0].y, "bf16")
+    phi, bias = dev(sets[0].phi), dev(sets[0].bias)
+    kw = dict(iters=sets[0].iters, eps=sets[0].eps, alphas=sets[0].alphas)
+    out_pre = (torch.empty((T, D), dtype=torch.bfloat16, device="cuda"), torch.empty((T, N), device="cuda"),
+               torch.empty((T, N), device="cuda"), torch.empty((T, N, N), device="cuda"))
+    out_pp = (torch.empty_like(x),) + tuple(torch.empty_like(t) for t in out_pre)
+    ws = torch.empty(mhc.workspace_bytes("pre", T, N, D, mhc.MHC_BF16), dtype=torch.uint8, device="cuda")
+    ws2 = torch.empty_like(ws)
+    mhc.mhc_pre(x, phi, bias, out=out_pre, workspace=ws, **kw)  # warm-up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ws.zero_()
+        mhc.mhc_pre(x, phi, bias, out=out_pre, workspace=ws, **kw)
+        ws2.zero_()
+        mhc.mhc_post_pre(x, y, Hq0, Hr0, phi, bias, out=out_pp, workspace=ws2, **kw)
+    for rep in range(6):
+        src = sets[rep % 3]
+        x.copy_(dev(src.x, "bf16"))
+        y.copy_(dev(src.y, "bf16"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref_pre = mhc.mhc_pre(x, phi, bias, **kw)
+        ref_pp = mhc.mhc_post_pre(x, y, Hq0, Hr0, phi, bias, **kw)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("h", "H_pre", "H_post", "H_res"), out_pre, ref_pre):
+            _bitwise(f"replay {rep} pre {name}", a, b)
+        for name, a, b in zip(NAMES, out_pp, ref_pp):
+            _bitwise(f"replay {rep} post_pre {name}", a, b)
