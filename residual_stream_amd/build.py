@@ -17,6 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmhc.so")
+ABI_RUN_SRC = os.path.join(os.path.dirname(HERE), "tests", "c", "mhc_abi_run.cpp")
+ABI_RUN = os.path.join(os.path.dirname(HERE), "tests", "c", "_build", "mhc_abi_run")
 
 SOURCES = ["mhc_api.cpp", "hc_pre.hip", "hc_pre_mfma.hip", "hc_post.hip", "hc_bwd.hip",
            "hc_pre_bwd_mfma.hip", "hc_pre_coop.hip", "hc_pre_decode.hip",
@@ -63,6 +65,10 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
     os.replace(tmp, LIB)
+    # the host-only program that drives the C ABI without Python (a GPU test runs it)
+    os.makedirs(os.path.dirname(ABI_RUN), exist_ok=True)
+    _run([cc, "-O2", "-std=c++17", f"-I{INCLUDE}", ABI_RUN_SRC, f"-L{HERE}", "-lmhc",
+          "-Wl,-rpath,$ORIGIN/../../../residual_stream_amd", "-o", ABI_RUN])
     if verbose:
         print(f"built {LIB}")
     return LIB
