@@ -295,6 +295,8 @@ def main():
         ts = sorted(a.elapsed_time(b) for a, b in evs)
         avg = sum(ts) / len(ts)
         per_call[name] = {"avg_us": avg * 1e3, "median_us": ts[len(ts) // 2] * 1e3,
+                          "p10_us": ts[int(0.1 * (len(ts) - 1))] * 1e3,
+                          "p90_us": ts[int(round(0.9 * (len(ts) - 1)))] * 1e3,
                           "algo_bytes": ab[name], "gbps": ab[name] / (avg * 1e-3) / 1e9}
 
     # forward pair alone (hc_pre + hc_post), the HBM-roofline headline
@@ -312,6 +314,28 @@ def main():
     fwd_ts = sorted(a.elapsed_time(b) for a, b in evs)
     fwd_ms = sum(fwd_ts) / len(fwd_ts)
     fwd_bytes = ab["mhc_pre"] + ab["mhc_post"]
+
+    def pct(ts, q):  # ts sorted
+        return ts[min(len(ts) - 1, max(0, int(round(q * (len(ts) - 1)))))]
+
+    # an on-box device copy moving the forward pair's byte count (half read,
+    # half written), HIP events, the same interleaving: the practical ceiling
+    # the forward is compared with besides the 8 TB/s peak
+    n_cp = fwd_bytes // 2 // 2  # bf16-sized elements read (and written) by the copy
+    cp_src = torch.ones(n_cp, dtype=torch.bfloat16, device=dev)
+    cp_dst = torch.empty_like(cp_src)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        cp_dst.copy_(cp_src)
+        evs[i][1].record(stream)
+        for _, f in calls:
+            f(sets[(i + 1) % 2])
+    torch.cuda.synchronize()
+    cp_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    copy_gbps = 2 * n_cp * 2 / (cp_ms * 1e-3) / 1e9
+    del cp_src, cp_dst
 
     # fused hc_post + next-layer hc_pre (one call per layer boundary), HIP
     # events, the rest of the step on the other input set in between
@@ -383,9 +407,13 @@ def main():
         "step_algo_bytes": step_bytes,
         "step_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
         "forward": {"calls": "mhc_pre + mhc_post", "avg_us": fwd_ms * 1e3,
+                    "median_us": pct(fwd_ts, 0.5) * 1e3, "p10_us": pct(fwd_ts, 0.1) * 1e3,
+                    "p90_us": pct(fwd_ts, 0.9) * 1e3,
                     "tokens_per_s": T / (fwd_ms * 1e-3), "algo_bytes": fwd_bytes,
                     "gbps": fwd_bytes / (fwd_ms * 1e-3) / 1e9,
-                    "frac_of_peak": fwd_bytes / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+                    "frac_of_peak": fwd_bytes / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                    "copy_gbps": copy_gbps,
+                    "frac_of_copy": fwd_bytes / (fwd_ms * 1e-3) / 1e9 / copy_gbps},
         "per_call": per_call,
         "post_pre_fused": {"call": "mhc_post_pre (hc_post of a layer + hc_pre of the next)",
                            "avg_us": pp_ms * 1e3, "algo_bytes": ab["mhc_post_pre"],
