@@ -219,25 +219,25 @@ def main():
                                     y_weight=True, out_weight=pn)
             ws_stab[(True, pn)] = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
 
-    def call_pre(st):
+    def call_pre(st, s=None):
         mhc.mhc_pre(st["x"], st["phi"], st["bias"], out=(st["h"], st["Hp"], st["Hq"], st["Hr"]),
-                    workspace=ws_pre_t, stream=stream, **kw)
+                    workspace=ws_pre_t, stream=s or stream, **kw)
 
-    def call_post(st):
-        mhc.mhc_post(st["x"], st["y"], st["Hq"], st["Hr"], out=st["xn"], stream=stream)
+    def call_post(st, s=None):
+        mhc.mhc_post(st["x"], st["y"], st["Hq"], st["Hr"], out=st["xn"], stream=s or stream)
 
-    def call_post_pre(st):
+    def call_post_pre(st, s=None):
         mhc.mhc_post_pre(st["x"], st["y"], st["Hq"], st["Hr"], st["phi"], st["bias"], out=st["f_out"],
-                         workspace=ws_pre_t, stream=stream, **kw)
+                         workspace=ws_pre_t, stream=s or stream, **kw)
 
-    def call_post_bwd(st):
+    def call_post_bwd(st, s=None):
         mhc.mhc_post_bwd(st["dxn"], st["x"], st["y"], st["Hq"], st["Hr"],
-                         out=(st["dx"], st["dy"], st["dHp"], st["dHr"]), stream=stream)
+                         out=(st["dx"], st["dy"], st["dHp"], st["dHr"]), stream=s or stream)
 
-    def call_pre_bwd(st):
+    def call_pre_bwd(st, s=None):
         mhc.mhc_pre_bwd(st["dh"], st["x"], st["phi"], st["bias"], st["dHp"], st["dHr"], st["dx"],
                         out=(st["dphi"], st["dbias"], st["dalpha"]), workspace=ws_bwd_t,
-                        stream=stream, **kw)
+                        stream=s or stream, **kw)
 
     def call_stable(st, pn):
         mhc.mhc_post_stable(st["x"], st["y"], st["Hq"], st["Hr"], y_weight=st["wy"],
@@ -274,6 +274,31 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
     print(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
+
+    # ---- the same step captured once per input set in a HIP graph and
+    # replayed: K replays between synchronisations, as above.  The graph also
+    # zero-fills the split-K hc_pre workspace before that call (a replay
+    # repeats the exchange tag drawn at capture, so records must start clear).
+    graphs = []
+    for s_idx in range(2):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream()
+            if ws_pre_t is not None:
+                ws_pre_t.zero_()
+            for _, f in calls:
+                f(sets[s_idx], cs)
+        graphs.append(g)
+    for i in range(args.warmup):
+        graphs[i % 2].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % 2].replay()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    del graphs
+    print(f"[bench] {args.steps} graph replays: {graph_ms:.4f} ms/step", file=sys.stderr, flush=True)
 
     # ---- per-call HIP-event timing (same stream), inputs alternating ----
     ab = algo_bytes(T, N, D, io)
@@ -404,6 +429,9 @@ def main():
         "config": {"workload": f"{args.workload}_fwd_bwd", "T": T, "N": N, "D": D, "io": io,
                    "sinkhorn_iters": 20, "alpha": 0.01,
                    "step": "mhc_pre + mhc_post + mhc_post_bwd + mhc_pre_bwd"},
+        "graph_step": {"ms_per_step": graph_ms, "tokens_per_s": T / (graph_ms * 1e-3),
+                       "note": "the same step replayed from a HIP graph (plus a zero fill of the "
+                               "split-K workspace)"},
         "step_algo_bytes": step_bytes,
         "step_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
         "forward": {"calls": "mhc_pre + mhc_post", "avg_us": fwd_ms * 1e3,
