@@ -76,6 +76,18 @@ CALL_KERNELS = {
     "mhc_post_stable_bwd_sw": ["post_stable_bwd<4, 1, 1, true, false>", "stable_wsum[grid=81920]"],
     "mhc_post_stable_bwd_both": ["post_stable_bwd<4, 1, 1, true, true>", "stable_wsum[grid=409600]"],
 }
+# the fp32 workloads (N = 4, D = 5120 or 2560) take the per-tile matrix-core
+# hc_pre (after packing φ) and the vector-ALU hc_pre backward
+CALL_KERNELS_F32 = {
+    "mhc_pre": ["phi_pack_kernel", "hc_pre_mfma_kernel"],
+    "mhc_post": ["hc_post_generic"],
+    "mhc_post_bwd": ["hc_post_bwd_generic"],
+    "mhc_pre_bwd": ["bwd_proj_f32_kernel", "bwd_coef_kernel", "bwd_dx_f32_kernel", "dphi_bias_sum_kernel"],
+    "mhc_post_stable_sw": ["post_stable_fwd"],
+    "mhc_post_stable_both": ["post_stable_fwd"],
+    "mhc_post_stable_bwd_sw": ["post_stable_bwd", "stable_wsum"],
+    "mhc_post_stable_bwd_both": ["post_stable_bwd", "stable_wsum"],
+}
 
 
 def kernel_source_hash():
@@ -87,9 +99,9 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel_call, src_hash):
+def load_traffic(kernel_call, src_hash, workload):
     """HBM traffic per launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel sources; else None."""
+    were taken on the current kernel sources and on this workload; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -97,7 +109,7 @@ def load_traffic(kernel_call, src_hash):
     except (OSError, ValueError):
         return None
     ent = doc.get(kernel_call)
-    if not ent or ent.get("source_hash") != src_hash:
+    if doc.get("workload") != workload or not ent or ent.get("source_hash") != src_hash:
         return None
     return ent.get("bytes_per_launch")
 
@@ -168,6 +180,7 @@ def main():
         return
     mhc.load()
     K, C = N * D, N * N + 2 * N
+    call_kernels = CALL_KERNELS if io == "bf16" else CALL_KERNELS_F32
     tdt = torch.bfloat16 if io == "bf16" else torch.float32
     kw = dict(iters=20, eps=1e-6, alphas=(0.01, 0.01, 0.01))
 
@@ -399,17 +412,17 @@ def main():
             gbps = ab[name] / (avg * 1e-3) / 1e9
             stabilised[name] = {"avg_us": avg * 1e3, "median_us": ts[len(ts) // 2] * 1e3,
                                 "algo_bytes": ab[name], "gbps": gbps, "frac_of_peak": gbps / HBM_PEAK_GBPS,
-                                "kernels": CALL_KERNELS[name]}
+                                "kernels": call_kernels[name]}
 
     # roofline: the single-kernel call that takes the most time in the step,
     # so that its event time is one kernel's duration (the rocprofv3 summary
     # lists the same kernel); the multi-kernel hc_pre backward is reported
     # beside it as the largest call
-    single = [k for k in per_call if len(CALL_KERNELS[k]) == 1]
+    single = [k for k in per_call if len(call_kernels[k]) == 1]
     dom = max(single, key=lambda k: per_call[k]["avg_us"])
     big = max(per_call, key=lambda k: per_call[k]["avg_us"])
     src_hash = kernel_source_hash()
-    traffic = load_traffic(dom, src_hash)
+    traffic = load_traffic(dom, src_hash, args.workload)
     achieved = per_call[dom]["gbps"]
     step_bytes = sum(ab[name] for name, _ in calls)
 
@@ -449,13 +462,13 @@ def main():
                            "frac_of_peak": ab["mhc_post_pre"] / (pp_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                            "separate_us": per_call["mhc_post"]["avg_us"] + per_call["mhc_pre"]["avg_us"]},
         "stabilised_write_back": stabilised,
-        "roofline": {"kernel": CALL_KERNELS[dom][0], "call": dom, "bound": "hbm",
+        "roofline": {"kernel": call_kernels[dom][0], "call": dom, "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "algo_bytes_per_launch": ab[dom], "avg_us": per_call[dom]["avg_us"]},
-        "largest_call": {"call": big, "kernels": CALL_KERNELS[big], "avg_us": per_call[big]["avg_us"],
+        "largest_call": {"call": big, "kernels": call_kernels[big], "avg_us": per_call[big]["avg_us"],
                          "achieved": per_call[big]["gbps"], "frac": per_call[big]["gbps"] / HBM_PEAK_GBPS,
-                         "traffic": load_traffic(big, src_hash), "algo_bytes_per_launch": ab[big]},
+                         "traffic": load_traffic(big, src_hash, args.workload), "algo_bytes_per_launch": ab[big]},
         "kernel_source_hash": src_hash,
     }
     if not args.no_cpu_baseline:
