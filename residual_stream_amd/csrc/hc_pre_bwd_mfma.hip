@@ -145,17 +145,11 @@ __global__ __launch_bounds__(64 * W, 1) void bwd_proj_kernel(
     hs[SL] = ld16(rh, gh);
   };
 
-  // The first kPRing − 1 blocks' loads go out first, so that x and dh stream
-  // while φ is staged (vector memory completes in order: the φ loads below
-  // arrive after them, and the block loop is entered with nothing outstanding).
-  // (kept in issue order: the wait counts in the loop assume slot 0 oldest)
-  unroll_slots<0, kPRing - 1>([&](auto sl) {
-    load_blk(decltype(sl)::value, sl);
-    __builtin_amdgcn_sched_barrier(0);
-  });
-
-  // φ: stream by stream through LDS (the red buffer), all global loads of a
-  // thread issued before the first LDS write
+  // φ: stream by stream through LDS (the red buffer).  Its global loads go out
+  // first, then those of the first kPRing − 1 blocks, so that x and dh stream
+  // while φ is staged: a CU's vector-memory path is the bottleneck here, and
+  // φ queued behind three blocks of x and dh would hold up the first block by
+  // their transfer time.
   uint4 bfr[kN][2];
   {
     constexpr int kV4 = kSl * kC / 4;  // float4 of one stream's slice rows
@@ -169,6 +163,12 @@ __global__ __launch_bounds__(64 * W, 1) void bwd_proj_kernel(
         f[n][k] = i < kV4 ? reinterpret_cast<const float4*>(phi + ((int64_t)n * D + slice * kSl) * kC)[i]
                           : make_float4(0.f, 0.f, 0.f, 0.f);
       }
+    __builtin_amdgcn_sched_barrier(0);
+    // (kept in issue order: the wait counts in the loop assume slot 0 oldest)
+    unroll_slots<0, kPRing - 1>([&](auto sl) {
+      load_blk(decltype(sl)::value, sl);
+      __builtin_amdgcn_sched_barrier(0);
+    });
     float* stage = &red[0][0][0][0];
     static_assert(kSl * kC <= 2 * W * 16 * kPartStride, "one stream's φ slice fits the red buffer");
 #pragma unroll
