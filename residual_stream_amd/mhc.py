@@ -156,6 +156,8 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
     kernel, recorded in the graph): the split-K hc_pre tags its exchange
     records with a number drawn at launch, which a replayed graph repeats, so
     each replay must start from records that match no tag."""
+    if torch.device(device).type != "cuda":
+        raise RuntimeError("the mHC kernels need GPU tensors (no CPU path)")
     if torch.cuda.is_current_stream_capturing():
         return torch.zeros(nbytes, dtype=torch.uint8, device=device)
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
