@@ -53,6 +53,11 @@ def algo_bytes(T, N, D, io):
         "mhc_post": T * (K * e + D * e + coef + K * e),
         "mhc_post_bwd": T * (3 * K * e + 2 * D * e + 2 * coef),
         "mhc_pre_bwd": T * (D * e + 3 * K * e + coef) + 2 * phi,
+        # the backward pair of the step: hc_post's backward without dx, then
+        # the hc_pre backward forming dx = H_resᵀ·dx_next + its own part
+        # (dx_next read where mhc_pre_bwd reads dx, and H_res)
+        "mhc_post_bwd_nodx": T * (2 * K * e + 2 * D * e + 2 * coef),
+        "mhc_pre_bwd_mix": T * (D * e + 3 * K * e + coef + N * N * 4) + 2 * phi,
         # hc_post(l) + hc_pre(l+1): x, y, H_post/H_res in; x_next, h, H out
         "mhc_post_pre": T * (K * e + D * e + coef + K * e + D * e + C * 4) + phi,
         # stabilised write-back: as mhc_post / mhc_post_bwd plus the norm
@@ -69,8 +74,10 @@ def algo_bytes(T, N, D, io):
 CALL_KERNELS = {
     "mhc_pre": ["hc_pre_coop_kernel"],
     "mhc_post": ["hc_post_generic"],
-    "mhc_post_bwd": ["hc_post_bwd_generic"],
-    "mhc_pre_bwd": ["bwd_proj_kernel", "bwd_coef_kernel", "bwd_dx_kernel", "dphi_bias_sum_kernel"],
+    "mhc_post_bwd": ["hc_post_bwd_generic<4, 1, true>"],
+    "mhc_pre_bwd": ["bwd_proj_kernel", "bwd_coef_kernel", "bwd_dx_kernel<false>", "dphi_bias_sum_kernel"],
+    "mhc_post_bwd_nodx": ["hc_post_bwd_generic<4, 1, false>"],
+    "mhc_pre_bwd_mix": ["bwd_proj_kernel", "bwd_coef_kernel", "bwd_dx_kernel<true>", "dphi_bias_sum_kernel"],
     "mhc_post_stable_sw": ["post_stable_fwd<4, 1, 1, true, false>"],
     "mhc_post_stable_both": ["post_stable_fwd<4, 1, 1, true, true>"],
     "mhc_post_stable_bwd_sw": ["post_stable_bwd<4, 1, 1, true, false>", "stable_wsum[grid=81920]"],
@@ -83,6 +90,9 @@ CALL_KERNELS_F32 = {
     "mhc_post": ["hc_post_generic"],
     "mhc_post_bwd": ["hc_post_bwd_generic"],
     "mhc_pre_bwd": ["bwd_proj_f32_kernel", "bwd_coef_kernel", "bwd_dx_f32_kernel", "dphi_bias_sum_kernel"],
+    "mhc_post_bwd_nodx": ["hc_post_bwd_generic"],
+    "mhc_pre_bwd_mix": ["res_mix_t_kernel", "bwd_proj_f32_kernel", "bwd_coef_kernel", "bwd_dx_f32_kernel",
+                        "dphi_bias_sum_kernel"],
     "mhc_post_stable_sw": ["post_stable_fwd"],
     "mhc_post_stable_both": ["post_stable_fwd"],
     "mhc_post_stable_bwd_sw": ["post_stable_bwd", "stable_wsum"],
@@ -247,6 +257,15 @@ def main():
         mhc.mhc_post_bwd(st["dxn"], st["x"], st["y"], st["Hq"], st["Hr"],
                          out=(st["dx"], st["dy"], st["dHp"], st["dHr"]), stream=s or stream)
 
+    def call_post_bwd_nodx(st, s=None):
+        mhc.mhc_post_bwd(st["dxn"], st["x"], st["y"], st["Hq"], st["Hr"],
+                         out=(None, st["dy"], st["dHp"], st["dHr"]), stream=s or stream)
+
+    def call_pre_bwd_mix(st, s=None):
+        mhc.mhc_pre_bwd_mix(st["dh"], st["x"], st["phi"], st["bias"], st["dHp"], st["dHr"], st["dxn"],
+                            st["Hr"], out=(st["dx"], st["dphi"], st["dbias"], st["dalpha"]),
+                            workspace=ws_bwd_t, stream=s or stream, **kw)
+
     def call_pre_bwd(st, s=None):
         mhc.mhc_pre_bwd(st["dh"], st["x"], st["phi"], st["bias"], st["dHp"], st["dHr"], st["dx"],
                         out=(st["dphi"], st["dbias"], st["dalpha"]), workspace=ws_bwd_t,
@@ -264,8 +283,12 @@ def main():
                                      st["dwx"] if pn else None),
                                 workspace=ws_stab[(True, pn)], stream=stream)
 
-    calls = [("mhc_pre", call_pre), ("mhc_post", call_post), ("mhc_post_bwd", call_post_bwd),
-             ("mhc_pre_bwd", call_pre_bwd)]
+    # the step: forward pair, then the backward pair with hc_post's share of
+    # dx formed inside the hc_pre backward; the two-call backward
+    # (mhc_post_bwd writing dx, mhc_pre_bwd adding into it) is timed beside it
+    calls = [("mhc_pre", call_pre), ("mhc_post", call_post), ("mhc_post_bwd_nodx", call_post_bwd_nodx),
+             ("mhc_pre_bwd_mix", call_pre_bwd_mix)]
+    ref_calls = [("mhc_post_bwd", call_post_bwd), ("mhc_pre_bwd", call_pre_bwd)]
 
     def step(i):
         st = sets[i % 2]
@@ -313,10 +336,20 @@ def main():
     del graphs
     print(f"[bench] {args.steps} graph replays: {graph_ms:.4f} ms/step", file=sys.stderr, flush=True)
 
+    # ---- the same step with the two-call backward ----
+    unfused = calls[:2] + ref_calls
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        for _, f in unfused:
+            f(sets[i % 2])
+    torch.cuda.synchronize()
+    unfused_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
     # ---- per-call HIP-event timing (same stream), inputs alternating ----
     ab = algo_bytes(T, N, D, io)
     per_call = {}
-    for name, f in calls:
+    for name, f in calls + ref_calls:
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
         for i in range(args.steps):
@@ -346,8 +379,8 @@ def main():
         call_pre(st)
         call_post(st)
         evs[i][1].record(stream)
-        call_post_bwd(sets[(i + 1) % 2])
-        call_pre_bwd(sets[(i + 1) % 2])
+        call_post_bwd_nodx(sets[(i + 1) % 2])
+        call_pre_bwd_mix(sets[(i + 1) % 2])
     torch.cuda.synchronize()
     fwd_ts = sorted(a.elapsed_time(b) for a, b in evs)
     fwd_ms = sum(fwd_ts) / len(fwd_ts)
@@ -441,7 +474,10 @@ def main():
         "data": "synthetic (seeded Gaussian x, y, dh, dx_next; phi ~ N(0, 1/(N*D)); bias ~ N(0, 0.1))",
         "config": {"workload": f"{args.workload}_fwd_bwd", "T": T, "N": N, "D": D, "io": io,
                    "sinkhorn_iters": 20, "alpha": 0.01,
-                   "step": "mhc_pre + mhc_post + mhc_post_bwd + mhc_pre_bwd"},
+                   "step": "mhc_pre + mhc_post + mhc_post_bwd (dy, dH; no dx) + mhc_pre_bwd_mix "
+                           "(dx = H_res^T dx_next + hc_pre part)"},
+        "two_call_backward_step": {"ms_per_step": unfused_ms, "tokens_per_s": T / (unfused_ms * 1e-3),
+                                   "step": "mhc_pre + mhc_post + mhc_post_bwd (writing dx) + mhc_pre_bwd"},
         "graph_step": {"ms_per_step": graph_ms, "tokens_per_s": T / (graph_ms * 1e-3),
                        "note": "the same step replayed from a HIP graph (plus a zero fill of the "
                                "split-K workspace)"},

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MHC_ABI_VERSION 2
+#define MHC_ABI_VERSION 3
 
 typedef enum mhc_dtype { MHC_F32 = 0, MHC_BF16 = 1 } mhc_dtype;
 
@@ -113,7 +113,11 @@ mhc_status mhc_post(const mhc_desc* desc, const void* x, const void* y, const fl
  *   dx[m]       = Σ_n H_res[n,m]·dx_next[n]        (I/O dtype, overwritten)
  *   dy          = Σ_n H_post[n]·dx_next[n]         (I/O dtype)
  *   dH_post[n]  = <dx_next[n], y>,  dH_res[n,m] = <dx_next[n], x[m]>   (fp32)
- * Must run before mhc_pre_bwd, which adds hc_pre's contribution into dx. */
+ * Must run before mhc_pre_bwd, which adds hc_pre's contribution into dx.
+ * dx may be NULL: nothing is written for it, and the caller passes dx_next
+ * and H_res to mhc_pre_bwd_mix instead, which forms the same term inside the
+ * hc_pre backward (the state gradient then crosses HBM once instead of being
+ * written here and read back there). */
 mhc_status mhc_post_bwd(const mhc_desc* desc, const void* dx_next, const void* x, const void* y,
                         const float* H_post, const float* H_res, void* dx, void* dy,
                         float* dH_post, float* dH_res, hipStream_t stream);
@@ -132,6 +136,22 @@ mhc_status mhc_pre_bwd(const mhc_desc* desc, const void* dh, const void* x, cons
                        const float* bias, const float* dH_post, const float* dH_res, void* dx,
                        float* dphi, float* dbias, float* dalpha, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
+
+/* mhc_pre_bwd with hc_post's share of the state gradient formed inside it:
+ *   dx = Σ_n H_res[n,m]·dx_next[n] + (the hc_pre part written by mhc_pre_bwd)
+ * (I/O dtype, overwritten).  For a block x → hc_pre → f → hc_post → x_next
+ * this is the state gradient mhc_post_bwd + mhc_pre_bwd produce together,
+ * with mhc_post_bwd called with dx = NULL; the H_res term is kept in fp32
+ * until the final rounding (bf16, N = 4, D % 256 == 0) or rounded once as
+ * mhc_post_bwd does (other shapes), so results agree with the two calls to
+ * rounding.  dphi, dbias and dalpha are exactly those of mhc_pre_bwd.
+ * dx_next and H_res are the arguments mhc_post_bwd took.  dx may be dx_next
+ * itself (the gradient is then formed in place), but must not overlap it
+ * otherwise, nor x or dh.  Same workspace as mhc_pre_bwd. */
+mhc_status mhc_pre_bwd_mix(const mhc_desc* desc, const void* dh, const void* x, const float* phi,
+                           const float* bias, const float* dH_post, const float* dH_res,
+                           const void* dx_next, const float* H_res, void* dx, float* dphi, float* dbias,
+                           float* dalpha, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* mhc_status_string(mhc_status status);

@@ -15,10 +15,14 @@ Triton article: only the hc_pre input x and the sublayer output y (plus the
 logits and the Sinkhorn rounds from x.  With ``recompute=True`` the sublayer is
 checkpointed too, so not even h or the sublayer's own activations are kept.
 
-The two backward calls share one dx buffer, as the C ABI intends: the hc_post
-backward writes its part of dx, and the hc_pre backward adds its own to it in
-place.  The hc_post node therefore hands its dx to the hc_pre node of the same
-block instead of returning it; the hc_pre node returns the total.
+The two backward nodes produce the state gradient together: the hc_post node
+computes dy and the coefficient gradients only (`mhc_post_bwd` without dx) and
+hands dx_next and H_res to the hc_pre node of the same block, whose
+`mhc_pre_bwd_mix` forms dx = H_resᵀ·dx_next plus its own part in one pass, so
+dx is written once instead of being written, read back and written again.
+(With the stabilised write-back the hc_post node writes its dx and hands that
+over; `mhc_pre_bwd` adds to it in place.)  The hc_post node therefore returns
+no gradient for x; the hc_pre node returns the total.
 
 openPangu's stabilised variant (openPangu 2.0 analysis, §5.4) is available
 through three switches: ``sandwich_norm`` (an RMSNorm with a learnable weight
@@ -48,12 +52,16 @@ from . import mhc
 
 
 class _DxHandoff:
-    """Carries hc_post's dx to the hc_pre backward of the same block."""
+    """Carries hc_post's share of the state gradient to the hc_pre backward of
+    the same block: either dx itself (stabilised write-back), or dx_next and
+    H_res, from which mhc_pre_bwd_mix forms it (plain write-back: dx then
+    crosses HBM once)."""
 
-    __slots__ = ("dx",)
+    __slots__ = ("dx", "mix")
 
     def __init__(self):
         self.dx = None
+        self.mix = None
 
 
 class _Pre(torch.autograd.Function):
@@ -72,9 +80,9 @@ class _Pre(torch.autograd.Function):
         x, phi, bias = ctx.saved_tensors
         iters, eps, alphas, want_dalpha = ctx.cfg
         T, N, D = x.shape
-        dx = ctx.handoff.dx
-        ctx.handoff.dx = None
-        if dx is None:  # hc_post's output took no gradient
+        dx, mix = ctx.handoff.dx, ctx.handoff.mix
+        ctx.handoff.dx = ctx.handoff.mix = None
+        if dx is None and mix is None:  # hc_post's output took no gradient
             dx = torch.zeros_like(x)
         if dh is None:
             dh = torch.zeros((T, D), dtype=x.dtype, device=x.device)
@@ -82,9 +90,15 @@ class _Pre(torch.autograd.Function):
             dHq = torch.zeros((T, N), dtype=torch.float32, device=x.device)
         if dHr is None:
             dHr = torch.zeros((T, N, N), dtype=torch.float32, device=x.device)
-        dx, dphi, dbias, dalpha = mhc.mhc_pre_bwd(
-            dh.contiguous(), x, phi, bias, dHq.contiguous(), dHr.contiguous(), dx,
-            iters=iters, eps=eps, alphas=alphas, want_dalpha=want_dalpha)
+        if mix is not None:
+            dx_next, H_res = mix
+            dx, dphi, dbias, dalpha = mhc.mhc_pre_bwd_mix(
+                dh.contiguous(), x, phi, bias, dHq.contiguous(), dHr.contiguous(), dx_next, H_res,
+                iters=iters, eps=eps, alphas=alphas, want_dalpha=want_dalpha)
+        else:
+            dx, dphi, dbias, dalpha = mhc.mhc_pre_bwd(
+                dh.contiguous(), x, phi, bias, dHq.contiguous(), dHr.contiguous(), dx,
+                iters=iters, eps=eps, alphas=alphas, want_dalpha=want_dalpha)
         dalpha = dalpha.cpu() if want_dalpha else None
         return dx, dphi, dbias, dalpha, None, None, None
 
@@ -106,13 +120,16 @@ class _Post(torch.autograd.Function):
     def backward(ctx, dx_next):
         x, y, H_post, H_res, y_weight, out_weight = ctx.saved_tensors
         if y_weight is None and out_weight is None:
-            dx, dy, dHq, dHr = mhc.mhc_post_bwd(dx_next.contiguous(), x, y, H_post, H_res)
+            # dx is formed by the hc_pre backward of this block from dx_next
+            dx_next = dx_next.contiguous()
+            _, dy, dHq, dHr = mhc.mhc_post_bwd(dx_next, x, y, H_post, H_res, want_dx=False)
+            ctx.handoff.mix = (dx_next, H_res)
             dyw = dow = None
         else:
             dx, dy, dHq, dHr, dyw, dow = mhc.mhc_post_stable_bwd(
                 dx_next.contiguous(), x, y, H_post, H_res, y_weight=y_weight,
                 out_weight=out_weight, eps=ctx.eps)
-        ctx.handoff.dx = dx  # the hc_pre backward of this block adds to it
+            ctx.handoff.dx = dx  # the hc_pre backward of this block adds to it
         return None, dy, dHq, dHr, dyw, dow, None, None
 
 
@@ -177,9 +194,10 @@ class _PostPre(torch.autograd.Function):
     """hc_post of block l fused with hc_pre of block l + 1 (`mhc_post_pre`).
 
     Backward, in the order the separate blocks run it: hc_pre's backward of
-    block l + 1 adds into the hc_post gradient of x_{l+1} that the next
-    boundary handed over, then hc_post's backward of block l; its dx goes to
-    the previous boundary (or block 0's hc_pre) through ``handoff_out``.
+    block l + 1 forms the gradient of x_{l+1} from the dx_next and H_res the
+    next boundary handed over, then hc_post's backward of block l runs without
+    dx and hands its own dx_next and H_res to the previous boundary (or block
+    0's hc_pre) through ``handoff_out``.
     """
 
     @staticmethod
@@ -198,23 +216,30 @@ class _PostPre(torch.autograd.Function):
         x, y, H_post_in, H_res_in, x_next, phi, bias = ctx.saved_tensors
         iters, eps, alphas, want_dalpha = ctx.cfg
         T, N, D = x.shape
-        dx_next = ctx.handoff_in.dx
-        ctx.handoff_in.dx = None
-        if dx_next is None:
-            dx_next = torch.zeros_like(x_next)
-        if dxn is not None:  # x_{l+1} also used outside the stack
-            dx_next = dx_next + dxn
         if dh is None:
             dh = torch.zeros((T, D), dtype=x.dtype, device=x.device)
         if dHq is None:
             dHq = torch.zeros((T, N), dtype=torch.float32, device=x.device)
         if dHr is None:
             dHr = torch.zeros((T, N, N), dtype=torch.float32, device=x.device)
-        dx_next, dphi, dbias, dalpha = mhc.mhc_pre_bwd(
-            dh.contiguous(), x_next, phi, bias, dHq.contiguous(), dHr.contiguous(), dx_next,
-            iters=iters, eps=eps, alphas=alphas, want_dalpha=want_dalpha)
-        dx, dy, dHq_in, dHr_in = mhc.mhc_post_bwd(dx_next, x, y, H_post_in, H_res_in)
-        ctx.handoff_out.dx = dx
+        kw = dict(iters=iters, eps=eps, alphas=alphas, want_dalpha=want_dalpha)
+        # hc_pre backward of block l + 1: the next boundary (or the last
+        # block's hc_post) handed over its dx_next and H_res, from which the
+        # state gradient of x_{l+1} is formed here
+        mix = ctx.handoff_in.mix
+        ctx.handoff_in.mix = None
+        if mix is not None:
+            dx_next, dphi, dbias, dalpha = mhc.mhc_pre_bwd_mix(
+                dh.contiguous(), x_next, phi, bias, dHq.contiguous(), dHr.contiguous(), mix[0], mix[1], **kw)
+        else:
+            dx_next, dphi, dbias, dalpha = mhc.mhc_pre_bwd(
+                dh.contiguous(), x_next, phi, bias, dHq.contiguous(), dHr.contiguous(),
+                torch.zeros_like(x_next), **kw)
+        if dxn is not None:  # x_{l+1} also used outside the stack
+            dx_next = dx_next + dxn
+        # hc_post backward of block l, its dx left to the previous boundary
+        _, dy, dHq_in, dHr_in = mhc.mhc_post_bwd(dx_next, x, y, H_post_in, H_res_in, want_dx=False)
+        ctx.handoff_out.mix = (dx_next, H_res_in)
         dalpha = dalpha.cpu() if want_dalpha else None
         return None, dy, dHq_in, dHr_in, dphi, dbias, dalpha, None, None, None, None
 

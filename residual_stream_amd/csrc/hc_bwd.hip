@@ -12,8 +12,9 @@ constexpr int kBwdThreads = 256;
 // ------------------------------------------------------------ hc_post bwd ---
 // One workgroup per token.  dx[m] = Σ_n H_res[n,m]·g[n], dy = Σ_n H_post[n]·g[n],
 // dH_res[n,m] = <g[n], x[m]>, dH_post[n] = <g[n], y>, with g = dx_next; the
-// N² + N sums in a fixed order.
-template <int N, int IO>
+// N² + N sums in a fixed order.  WDX = false leaves dx to the caller's hc_pre
+// backward (mhc_pre_bwd_mix forms it from dx_next there).
+template <int N, int IO, bool WDX>
 __global__ __launch_bounds__(kBwdThreads) void hc_post_bwd_generic(
     const void* __restrict__ dxn, const void* __restrict__ x, const void* __restrict__ y,
     const float* __restrict__ H_post, const float* __restrict__ H_res, void* __restrict__ dx,
@@ -41,17 +42,19 @@ __global__ __launch_bounds__(kBwdThreads) void hc_post_bwd_generic(
       load8<IO>(dxn, xb + (int64_t)n * D + d0, g[n]);
       load8<IO>(x, xb + (int64_t)n * D + d0, xv[n]);
     }
+    if constexpr (WDX) {
 #pragma unroll
-    for (int m = 0; m < N; ++m) {
-      float o[8];
+      for (int m = 0; m < N; ++m) {
+        float o[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float a = 0.f;
+        for (int j = 0; j < 8; ++j) {
+          float a = 0.f;
 #pragma unroll
-        for (int n = 0; n < N; ++n) a += hr[n][m] * g[n][j];
-        o[j] = a;
+          for (int n = 0; n < N; ++n) a += hr[n][m] * g[n][j];
+          o[j] = a;
+        }
+        store8<IO>(dx, xb + (int64_t)m * D + d0, o);
       }
-      store8<IO>(dx, xb + (int64_t)m * D + d0, o);
     }
     float o[8];
 #pragma unroll
@@ -97,8 +100,59 @@ hipError_t launch_post_bwd(const mhc_desc& d, const void* dxn, const void* x, co
     dispatch_io(d.io, [&](auto io_) {
       constexpr int N = decltype(n_)::value;
       constexpr int IO = decltype(io_)::value;
-      hipLaunchKernelGGL((hc_post_bwd_generic<N, IO>), dim3((unsigned)d.T), dim3(kBwdThreads), 0,
-                         s, dxn, x, y, H_post, H_res, dx, dy, dH_post, dH_res, d.D);
+      if (dx != nullptr)
+        hipLaunchKernelGGL((hc_post_bwd_generic<N, IO, true>), dim3((unsigned)d.T), dim3(kBwdThreads), 0,
+                           s, dxn, x, y, H_post, H_res, dx, dy, dH_post, dH_res, d.D);
+      else
+        hipLaunchKernelGGL((hc_post_bwd_generic<N, IO, false>), dim3((unsigned)d.T), dim3(kBwdThreads),
+                           0, s, dxn, x, y, H_post, H_res, dx, dy, dH_post, dH_res, d.D);
+    });
+  });
+  if (!ok) return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// dx[m] = Σ_n H_res[n,m]·dx_next[n] alone (one workgroup per token), in the
+// arithmetic of hc_post_bwd_generic: the hc_post part of the state gradient
+// for shapes whose hc_pre backward does not form it itself.
+template <int N, int IO>
+__global__ __launch_bounds__(kBwdThreads) void res_mix_t_kernel(const void* __restrict__ dxn,
+                                                               const float* __restrict__ H_res,
+                                                               void* __restrict__ dx, int D) {
+  const int64_t t = blockIdx.x;
+  float hr[N][N];
+#pragma unroll
+  for (int n = 0; n < N; ++n)
+#pragma unroll
+    for (int m = 0; m < N; ++m) hr[n][m] = H_res[(t * N + n) * N + m];
+  const int64_t xb = t * (int64_t)N * D;
+  for (int d0 = threadIdx.x * 8; d0 < D; d0 += kBwdThreads * 8) {
+    float g[N][8];
+#pragma unroll
+    for (int n = 0; n < N; ++n) load8<IO>(dxn, xb + (int64_t)n * D + d0, g[n]);
+#pragma unroll
+    for (int m = 0; m < N; ++m) {
+      float o[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float a = 0.f;
+#pragma unroll
+        for (int n = 0; n < N; ++n) a += hr[n][m] * g[n][j];
+        o[j] = a;
+      }
+      store8<IO>(dx, xb + (int64_t)m * D + d0, o);
+    }
+  }
+}
+
+static hipError_t launch_res_mix_t(const mhc_desc& d, const void* dxn, const float* H_res, void* dx,
+                                   hipStream_t s) {
+  bool ok = dispatch_n(d.N, [&](auto n_) {
+    dispatch_io(d.io, [&](auto io_) {
+      constexpr int N = decltype(n_)::value;
+      constexpr int IO = decltype(io_)::value;
+      hipLaunchKernelGGL((res_mix_t_kernel<N, IO>), dim3((unsigned)d.T), dim3(kBwdThreads), 0, s, dxn,
+                         H_res, dx, d.D);
     });
   });
   if (!ok) return hipErrorInvalidValue;
@@ -372,11 +426,26 @@ __global__ __launch_bounds__(kBwdThreads) void bias_alpha_reduce(const float* __
   }
 }
 
+hipError_t launch_pre_bwd_mix(const mhc_desc& d, const void* dh, const void* x, const float* phi,
+                              const float* bias, const float* dH_post, const float* dH_res,
+                              const void* dxn, const float* H_res, void* dx, float* dphi, float* dbias,
+                              float* dalpha, void* ws, hipStream_t s) {
+  // bf16 on the matrix-core path: the dx pass reads dx_next and mixes it in
+  // registers; elsewhere the mix is written first and accumulated into
+  if (pre_bwd_mfma_eligible(d) && d.io == kBF16)
+    return launch_pre_bwd_mfma(d, dh, x, phi, bias, dH_post, dH_res, dx, dphi, dbias, dalpha, ws, s, dxn,
+                               H_res);
+  const hipError_t e = launch_res_mix_t(d, dxn, H_res, dx, s);
+  if (e != hipSuccess) return e;
+  return launch_pre_bwd(d, dh, x, phi, bias, dH_post, dH_res, dx, dphi, dbias, dalpha, ws, s);
+}
+
 hipError_t launch_pre_bwd(const mhc_desc& d, const void* dh, const void* x, const float* phi,
                           const float* bias, const float* dH_post, const float* dH_res, void* dx,
                           float* dphi, float* dbias, float* dalpha, void* ws, hipStream_t s) {
   if (pre_bwd_mfma_eligible(d)) {
-    return launch_pre_bwd_mfma(d, dh, x, phi, bias, dH_post, dH_res, dx, dphi, dbias, dalpha, ws, s);
+    return launch_pre_bwd_mfma(d, dh, x, phi, bias, dH_post, dH_res, dx, dphi, dbias, dalpha, ws, s,
+                               nullptr, nullptr);
   }
   const PreBwdLayout L = pre_bwd_layout(d);
   char* w = static_cast<char*>(ws);

@@ -472,6 +472,11 @@ __global__ __launch_bounds__(kCoefThreads) void bwd_coef_kernel(
 // The next tile's x, dx, dh and coefficients are loaded while a tile is
 // worked on (two register buffers; vector memory completes in order, so those
 // loads never wait on the stores issued after them).
+// MIX: the kernel reads dx_next and H_res instead of dx and writes
+// dx = H_resᵀ·dx_next + dx̄ − β·x + H_pre[n]·dh, the hc_post part formed in
+// fp32 (the four streams of a piece's token and d-chunk sit in lanes
+// pc + 16n of the same wave: lanes l ^ 16, l ^ 32, l ^ 48, reached with the
+// permlane swaps).
 constexpr int kDxThreads = 256;
 constexpr int kDxWd = 128;        // d per stream per slice
 constexpr int kDxK = kN * kDxWd;  // 512 k per slice
@@ -483,14 +488,29 @@ constexpr int kTRow = 24;         // bf16 per Gᵀ row (16 t + pad)
 constexpr int kHRow = kDxWd + 8;  // bf16 per dh row
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// v of lane l ^ 16 and of lane l ^ 32 (v_permlane16_swap / v_permlane32_swap
+// with both operands v: the first result keeps the even rows or the low half
+// and receives the partner's value in the others, the second the reverse).
+// Every lane of the wave must be active.
+__device__ __forceinline__ uint32_t lane_xor16(uint32_t v, bool even_row) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return even_row ? r[1] : r[0];
+}
+__device__ __forceinline__ uint32_t lane_xor32(uint32_t v, bool low_half) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return low_half ? r[1] : r[0];
+}
 __device__ __forceinline__ f32x4_t mfma16(s16x4_t a, s16x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
+template <bool MIX>
 __global__ __launch_bounds__(kDxThreads, 2) void bwd_dx_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ dh, const float* __restrict__ phi,
     const float* __restrict__ coef, uint16_t* __restrict__ dx, float* __restrict__ dphi_part,
-    int64_t T, int D, int64_t tok_per_split) {
+    int64_t T, int D, int64_t tok_per_split, const uint16_t* __restrict__ dxn,
+    const float* __restrict__ hres) {
   __shared__ __align__(16) uint16_t xs[kDxTile * kXRow];     // x[t][k] of the tile
   __shared__ __align__(16) float dxr[kDxTile * kRRow];       // (G·φᵀ)[t][k]
   __shared__ __align__(16) uint16_t Gs[kDxTile * kGRow];     // G[t][c]
@@ -498,6 +518,7 @@ __global__ __launch_bounds__(kDxThreads, 2) void bwd_dx_kernel(
   __shared__ __align__(16) uint16_t hs[2][kDxTile * kHRow];  // dh[t][d], by tile parity
   __shared__ float bs[2][kDxTile];                           // β, by tile parity
   __shared__ __align__(16) float hps[2][kDxTile][kN];        // H_pre, by tile parity
+  __shared__ __align__(16) float hrs[MIX ? 2 : 1][kDxTile][kN * kN];  // H_res (MIX), by tile parity
 
   const int K = kN * D;
   const int d_base = blockIdx.x * kDxWd;
@@ -544,6 +565,11 @@ __global__ __launch_bounds__(kDxThreads, 2) void bwd_dx_kernel(
   // 128..143 [β, H_pre 0..2] and 144..159 [H_pre 3, -] of token tid mod 16
   const int ct = tid < 128 ? tid >> 3 : tid & 15;
   const int cc = tid < 128 ? 4 * (tid & 7) : (tid < 144 ? 32 : 36);
+  // MIX: the last wave loads the tile's H_res, lane l row l mod 4 of token
+  // l / 4 (the other waves issue no load for it)
+  static_assert(4 * kDxTile == kWave && kDxThreads / kWave == 4, "one H_res row per lane of wave 3");
+  const bool hr_wave = __builtin_amdgcn_readfirstlane(wave) == 3;
+  const uint32_t hr_off = (uint32_t)(lane * 16);
 
   auto rows_in = [&](int64_t t0) -> uint32_t {
     const int64_t r = te - t0;
@@ -551,6 +577,7 @@ __global__ __launch_bounds__(kDxThreads, 2) void bwd_dx_kernel(
   };
   uint4 bx[2][4], bd[2][4], bh[2];
   float4 bc[2];
+  uint4 bq[2];  // MIX: an H_res row
   // raw loads only: a value computed from a load here would make the wave wait
   // for it, and so for every load issued before it
   auto load_tile = [&](int64_t t0, auto slot_c) {
@@ -558,7 +585,7 @@ __global__ __launch_bounds__(kDxThreads, 2) void bwd_dx_kernel(
     const uint32_t rows = rows_in(t0);
     const int64_t tbase = rows > 0 ? t0 : 0;
     const auto rx = make_rsrc(x + tbase * K, rows * (uint32_t)K * 2);
-    const auto rd = make_rsrc(dx + tbase * K, rows * (uint32_t)K * 2);
+    const auto rd = make_rsrc((MIX ? dxn : dx) + tbase * K, rows * (uint32_t)K * 2);
     const auto rh = make_rsrc(dh + tbase * D, rows * (uint32_t)D * 2);
     const auto rc = make_rsrc(coef + tbase * kCoefStride, rows * (uint32_t)kCoefStride * 4);
 #pragma unroll
@@ -569,6 +596,12 @@ __global__ __launch_bounds__(kDxThreads, 2) void bwd_dx_kernel(
     const uint4 cv = ld16(rc, (uint32_t)((ct * kCoefStride + cc) * 4));
     bc[SL] = make_float4(__uint_as_float(cv.x), __uint_as_float(cv.y), __uint_as_float(cv.z),
                          __uint_as_float(cv.w));
+    if constexpr (MIX) {
+      if (hr_wave) {
+        const auto rr = make_rsrc(hres + tbase * kN * kN, rows * (uint32_t)(kN * kN * 4));
+        bq[SL] = ld16(rr, hr_off);
+      }
+    }
   };
 
   auto tile = [&](int64_t t0, auto slot_c) {
@@ -596,6 +629,9 @@ __global__ __launch_bounds__(kDxThreads, 2) void bwd_dx_kernel(
       } else if (tid < 160) {
         hps[SL][ct][3] = v.x;
       }
+    }
+    if constexpr (MIX) {
+      if (hr_wave) *reinterpret_cast<uint4*>(&hrs[SL][lane >> 2][4 * (lane & 3)]) = bq[SL];
     }
     // ---- the next tile into the other buffer
     load_tile(t0 + kDxTile, std::integral_constant<int, SL ^ 1>{});
@@ -637,11 +673,41 @@ __global__ __launch_bounds__(kDxThreads, 2) void bwd_dx_kernel(
       const uint4 xv = bx[SL][j], dv = bd[SL][j];
       const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, hw[4] = {hv.x, hv.y, hv.z, hv.w},
                      dw[4] = {dv.x, dv.y, dv.z, dv.w};
+      // the hc_post part of the piece: dx_next itself, or (MIX) column pn of
+      // H_res applied to the token's four streams
+      float base[8];
+      if constexpr (MIX) {
+        // stream pn ^ k sits in lane l ^ 16k: sum over k = 0..3 (this lane's
+        // stream first), H_res[t][pn ^ k][pn]·dx_next[pn ^ k]
+        const bool even_row = (lane & 16) == 0, low_half = lane < 32;
+        float hk[kN];
+#pragma unroll
+        for (int k = 0; k < kN; ++k) hk[k] = hrs[SL][t][(pn ^ k) * kN + pn];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t w1 = lane_xor16(dw[q], even_row);
+          const uint32_t gk[kN] = {dw[q], w1, lane_xor32(dw[q], low_half), lane_xor32(w1, low_half)};
+          float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+          for (int k = 0; k < kN; ++k) {
+            a0 += hk[k] * bf16_lo(gk[k]);
+            a1 += hk[k] * bf16_hi(gk[k]);
+          }
+          base[2 * q] = a0;
+          base[2 * q + 1] = a1;
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          base[2 * q] = bf16_lo(dw[q]);
+          base[2 * q + 1] = bf16_hi(dw[q]);
+        }
+      }
       uint32_t ow[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float o0 = bf16_lo(dw[q]) + rv[2 * q] - beta * bf16_lo(xw[q]) + hp * bf16_lo(hw[q]);
-        const float o1 = bf16_hi(dw[q]) + rv[2 * q + 1] - beta * bf16_hi(xw[q]) + hp * bf16_hi(hw[q]);
+        const float o0 = base[2 * q] + rv[2 * q] - beta * bf16_lo(xw[q]) + hp * bf16_lo(hw[q]);
+        const float o1 = base[2 * q + 1] + rv[2 * q + 1] - beta * bf16_hi(xw[q]) + hp * bf16_hi(hw[q]);
         ow[q] = pack_bf16x2(o0, o1);
       }
       st16(ro, vo[j], make_uint4(ow[0], ow[1], ow[2], ow[3]));
@@ -1109,7 +1175,8 @@ size_t pre_bwd_mfma_workspace_bytes(const mhc_desc& d) { return bwdm::layout(d).
 hipError_t launch_pre_bwd_mfma(const mhc_desc& d, const void* dh, const void* x, const float* phi,
                                const float* bias, const float* dH_post, const float* dH_res,
                                void* dx, float* dphi, float* dbias, float* dalpha, void* ws,
-                               hipStream_t s) {
+                               hipStream_t s, const void* dxn, const float* H_res) {
+  if (dxn != nullptr && d.io != kBF16) return hipErrorInvalidValue;  // the fp32 passes do not mix
   using namespace bwdm;
   const Layout L = layout(d);
   char* w = static_cast<char*>(ws);
@@ -1142,10 +1209,15 @@ hipError_t launch_pre_bwd_mfma(const mhc_desc& d, const void* dh, const void* x,
     hipLaunchKernelGGL(bwd_dx_f32_kernel, dim3((unsigned)(d.D / kFD), (unsigned)L.TS), dim3(kFThreads), 0, s,
                        static_cast<const float*>(x), static_cast<const float*>(dh), phi, coef,
                        static_cast<float*>(dx), dphi_part, T, d.D, tps);
+  else if (dxn != nullptr)
+    hipLaunchKernelGGL(bwd_dx_kernel<true>, dim3((unsigned)(K / kDxK), (unsigned)L.TS), dim3(kDxThreads), 0,
+                       s, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dh), phi, coef,
+                       static_cast<uint16_t*>(dx), dphi_part, T, d.D, tps, static_cast<const uint16_t*>(dxn),
+                       H_res);
   else
-    hipLaunchKernelGGL(bwd_dx_kernel, dim3((unsigned)(K / kDxK), (unsigned)L.TS), dim3(kDxThreads), 0, s,
-                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dh), phi, coef,
-                       static_cast<uint16_t*>(dx), dphi_part, T, d.D, tps);
+    hipLaunchKernelGGL(bwd_dx_kernel<false>, dim3((unsigned)(K / kDxK), (unsigned)L.TS), dim3(kDxThreads), 0,
+                       s, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dh), phi, coef,
+                       static_cast<uint16_t*>(dx), dphi_part, T, d.D, tps, nullptr, nullptr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t KC = (int64_t)K * kC;
   hipLaunchKernelGGL(dphi_bias_sum_kernel, dim3((unsigned)((KC + 255) / 256 + 1)), dim3(256), 0, s,

@@ -128,15 +128,17 @@ mhc_status mhc_post_bwd(const mhc_desc* d, const void* dx_next, const void* x, c
                         float* dH_post, float* dH_res, hipStream_t stream) {
   mhc_status st = check_desc(d);
   if (st != MHC_OK) return st;
+  // dx may be null: the caller then forms it in mhc_pre_bwd_mix
   if (!aligned16(dx_next) || !aligned16(x) || !aligned16(y) || !aligned16(H_post) ||
-      !aligned16(H_res) || !aligned16(dx) || !aligned16(dy) || !aligned16(dH_post) ||
+      !aligned16(H_res) || (dx != nullptr && !aligned16(dx)) || !aligned16(dy) || !aligned16(dH_post) ||
       !aligned16(dH_res))
     return MHC_ERR_INVALID_ARG;
   const size_t b = io_bytes(d), T = (size_t)d->T, N = (size_t)d->N, D = (size_t)d->D;
   const size_t big = T * N * D * b, small = T * D * b;
-  if (overlaps(dx, big, dx_next, big) || overlaps(dx, big, x, big) || overlaps(dx, big, y, small) ||
-      overlaps(dy, small, dx_next, big) || overlaps(dy, small, x, big) || overlaps(dy, small, dx, big))
+  if (dx != nullptr && (overlaps(dx, big, dx_next, big) || overlaps(dx, big, x, big) ||
+                        overlaps(dx, big, y, small) || overlaps(dy, small, dx, big)))
     return MHC_ERR_INVALID_ARG;
+  if (overlaps(dy, small, dx_next, big) || overlaps(dy, small, x, big)) return MHC_ERR_INVALID_ARG;
   return from_hip(
       mhc::launch_post_bwd(*d, dx_next, x, y, H_post, H_res, dx, dy, dH_post, dH_res, stream));
 }
@@ -160,6 +162,30 @@ mhc_status mhc_pre_bwd(const mhc_desc* d, const void* dh, const void* x, const f
     return MHC_ERR_INVALID_ARG;
   return from_hip(mhc::launch_pre_bwd(*d, dh, x, phi, bias, dH_post, dH_res, dx, dphi, dbias,
                                       dalpha, workspace, stream));
+}
+
+mhc_status mhc_pre_bwd_mix(const mhc_desc* d, const void* dh, const void* x, const float* phi,
+                           const float* bias, const float* dH_post, const float* dH_res,
+                           const void* dx_next, const float* H_res, void* dx, float* dphi, float* dbias,
+                           float* dalpha, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  mhc_status st = check_desc(d);
+  if (st != MHC_OK) return st;
+  if (d->sinkhorn_iters > kMaxBwdIters) return MHC_ERR_UNSUPPORTED;
+  if (!aligned16(dh) || !aligned16(x) || !aligned16(phi) || !aligned16(bias) ||
+      !aligned16(dH_post) || !aligned16(dH_res) || !aligned16(dx_next) || !aligned16(H_res) ||
+      !aligned16(dx) || !aligned16(dphi) || !aligned16(dbias))
+    return MHC_ERR_INVALID_ARG;
+  if (dalpha != nullptr && (reinterpret_cast<uintptr_t>(dalpha) & 3u) != 0) return MHC_ERR_INVALID_ARG;
+  const size_t b = io_bytes(d), T = (size_t)d->T, N = (size_t)d->N, D = (size_t)d->D;
+  const size_t big = T * N * D * b, small = T * D * b;
+  // dx may be dx_next itself (updated in place), but not overlap it otherwise
+  if (overlaps(dx, big, x, big) || overlaps(dx, big, dh, small) ||
+      (dx != dx_next && overlaps(dx, big, dx_next, big)))
+    return MHC_ERR_INVALID_ARG;
+  if (!workspace_ok(workspace, workspace_bytes, mhc::pre_bwd_workspace_bytes(*d)))
+    return MHC_ERR_INVALID_ARG;
+  return from_hip(mhc::launch_pre_bwd_mix(*d, dh, x, phi, bias, dH_post, dH_res, dx_next, H_res, dx, dphi,
+                                          dbias, dalpha, workspace, stream));
 }
 
 size_t mhc_post_pre_workspace_bytes(const mhc_desc* d) {

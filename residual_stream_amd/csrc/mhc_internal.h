@@ -67,12 +67,18 @@ size_t pre_bwd_workspace_bytes(const mhc_desc& d);
 // per-token dℓ and dα terms in the workspace for the shared bias/α reduction.
 bool pre_bwd_mfma_eligible(const mhc_desc& d);
 size_t pre_bwd_mfma_workspace_bytes(const mhc_desc& d);
+// With dxn and H_res non-null (bf16 only) the dx pass writes
+// dx = H_resᵀ·dx_next + the hc_pre part instead of accumulating into dx.
 hipError_t launch_pre_bwd_mfma(const mhc_desc& d, const void* dh, const void* x, const float* phi,
                                const float* bias, const float* dH_post, const float* dH_res,
                                void* dx, float* dphi, float* dbias, float* dalpha, void* ws,
-                               hipStream_t s);
+                               hipStream_t s, const void* dxn, const float* H_res);
 hipError_t launch_pre_bwd(const mhc_desc& d, const void* dh, const void* x, const float* phi,
                           const float* bias, const float* dH_post, const float* dH_res, void* dx,
                           float* dphi, float* dbias, float* dalpha, void* ws, hipStream_t s);
+hipError_t launch_pre_bwd_mix(const mhc_desc& d, const void* dh, const void* x, const float* phi,
+                              const float* bias, const float* dH_post, const float* dH_res,
+                              const void* dxn, const float* H_res, void* dx, float* dphi, float* dbias,
+                              float* dalpha, void* ws, hipStream_t s);
 
 }  // namespace mhc

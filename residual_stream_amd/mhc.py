@@ -31,6 +31,7 @@ ABI_FUNCTIONS = (
     "mhc_post_bwd",
     "mhc_pre_bwd_workspace_bytes",
     "mhc_pre_bwd",
+    "mhc_pre_bwd_mix",
     "mhc_post_pre_workspace_bytes",
     "mhc_post_pre",
     "mhc_post_stable",
@@ -91,6 +92,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.mhc_post_bwd.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.mhc_pre_bwd.restype = ctypes.c_int
     lib.mhc_pre_bwd.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.mhc_pre_bwd_mix.restype = ctypes.c_int
+    lib.mhc_pre_bwd_mix.argtypes = [_DP] + [_P] * 13 + [ctypes.c_size_t, _P]
     lib.mhc_post_pre.restype = ctypes.c_int
     lib.mhc_post_pre.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.mhc_post_stable.restype = ctypes.c_int
@@ -204,13 +207,15 @@ def mhc_post(x, y, H_post, H_res, *, out=None, stream=None):
     return out
 
 
-def mhc_post_bwd(dx_next, x, y, H_post, H_res, *, out=None, stream=None):
-    """hc_post backward: returns (dx[T,N,D], dy[T,D], dH_post[T,N], dH_res[T,N,N])."""
+def mhc_post_bwd(dx_next, x, y, H_post, H_res, *, want_dx=True, out=None, stream=None):
+    """hc_post backward: returns (dx[T,N,D], dy[T,D], dH_post[T,N], dH_res[T,N,N]).
+    With want_dx=False (or a None dx in `out`) dx is not formed (None is
+    returned in its place): :func:`mhc_pre_bwd_mix` forms it from dx_next."""
     lib = load()
     d = desc_for(x)
     T, N, D = x.shape
     if out is None:
-        out = (torch.empty_like(x), torch.empty_like(y),
+        out = (torch.empty_like(x) if want_dx else None, torch.empty_like(y),
                torch.empty((T, N), dtype=torch.float32, device=x.device),
                torch.empty((T, N, N), dtype=torch.float32, device=x.device))
     dx, dy, dHp, dHr = out
@@ -245,6 +250,34 @@ def mhc_pre_bwd(dh, x, phi, bias, dH_post, dH_res, dx, *, iters=20, eps=1e-6,
                          _ptr(_f32(dH_post)), _ptr(_f32(dH_res)), _ptr(dx), _ptr(dphi),
                          _ptr(dbias), _ptr(dalpha), _ptr(workspace), nbytes, _stream(stream))
     _check(st, "mhc_pre_bwd")
+    return dx, dphi, dbias, (dalpha[:3] if dalpha is not None else None)
+
+
+def mhc_pre_bwd_mix(dh, x, phi, bias, dH_post, dH_res, dx_next, H_res, *, iters=20, eps=1e-6,
+                    alphas=(0.01, 0.01, 0.01), want_dalpha=True, out=None, workspace=None, stream=None):
+    """hc_pre backward with hc_post's share of the state gradient formed
+    inside it: dx = H_resᵀ·dx_next + the hc_pre part (pair with
+    ``mhc_post_bwd(..., want_dx=False)``).
+
+    Returns (dx[T,N,D], dphi[K,C], dbias[C], dalpha[3] or None)."""
+    lib = load()
+    d = desc_for(x, iters, eps, alphas)
+    T, N, D = x.shape
+    C = N * N + 2 * N
+    if out is None:
+        out = (torch.empty_like(x), torch.empty((N * D, C), dtype=torch.float32, device=x.device),
+               torch.empty((C,), dtype=torch.float32, device=x.device),
+               torch.empty((4,), dtype=torch.float32, device=x.device) if want_dalpha else None)
+    dx, dphi, dbias, dalpha = out
+    need = lib.mhc_pre_bwd_workspace_bytes(ctypes.byref(d))
+    if workspace is None and need:
+        workspace = _workspace(need, x.device)
+    nbytes = workspace.numel() if workspace is not None else 0
+    st = lib.mhc_pre_bwd_mix(ctypes.byref(d), _ptr(dh), _ptr(x), _ptr(_f32(phi)), _ptr(_f32(bias)),
+                             _ptr(_f32(dH_post)), _ptr(_f32(dH_res)), _ptr(dx_next), _ptr(_f32(H_res)),
+                             _ptr(dx), _ptr(dphi), _ptr(dbias), _ptr(dalpha), _ptr(workspace), nbytes,
+                             _stream(stream))
+    _check(st, "mhc_pre_bwd_mix")
     return dx, dphi, dbias, (dalpha[:3] if dalpha is not None else None)
 
 

@@ -43,9 +43,12 @@ def _load(bufs, src, io):
 STEP_CASES = [("bf16", 4, 5120, 300), ("f32", 4, 2560, 70), ("bf16", 2, 512, 33)]
 
 
+@pytest.mark.parametrize("mix", [False, True], ids=["two_call_bwd", "mix_bwd"])
 @pytest.mark.parametrize("io,N,D,T", STEP_CASES)
-def test_training_step_graph_replays_match_eager(io, N, D, T):
-    _say(f"[graph] step {io} N={N} D={D} T={T}")
+def test_training_step_graph_replays_match_eager(io, N, D, T, mix):
+    # mix: mhc_post_bwd without dx, then mhc_pre_bwd_mix (the backward pair
+    # the benchmark's step uses); else mhc_post_bwd then mhc_pre_bwd
+    _say(f"[graph] step {io} N={N} D={D} T={T} mix={mix}")
     sets = [make_inputs(T, N, D, io=io, seed=100 + s, alpha=0.3, grads=True) for s in range(3)]
     s0 = sets[0]
     kw = dict(iters=s0.iters, eps=s0.eps, alphas=s0.alphas)
@@ -65,12 +68,19 @@ def test_training_step_graph_replays_match_eager(io, N, D, T):
     ws_bwd = torch.empty(max(mhc.workspace_bytes("pre_bwd", T, N, D, mhc._io_of(x)), 1), dtype=torch.uint8,
                          device="cuda")
 
+    def backward(Hq, Hr, pb, qb, ws):
+        if mix:
+            mhc.mhc_post_bwd(dxn, x, y, Hq, Hr, out=(None,) + tuple(pb[1:]))
+            return mhc.mhc_pre_bwd_mix(dh, x, phi, bias, pb[2], pb[3], dxn, Hr, out=(pb[0],) + tuple(qb),
+                                       workspace=ws, **kw)
+        mhc.mhc_post_bwd(dxn, x, y, Hq, Hr, out=pb)
+        return mhc.mhc_pre_bwd(dh, x, phi, bias, pb[2], pb[3], pb[0], out=qb, workspace=ws, **kw)
+
     def step():
         ws_pre.zero_()
         h, Hp, Hq, Hr = mhc.mhc_pre(x, phi, bias, out=pre_out, workspace=ws_pre, **kw)
         mhc.mhc_post(x, y, Hq, Hr, out=xn)
-        dx, dy, dHq, dHr = mhc.mhc_post_bwd(dxn, x, y, Hq, Hr, out=pb_out)
-        mhc.mhc_pre_bwd(dh, x, phi, bias, dHq, dHr, dx, out=qb_out, workspace=ws_bwd, **kw)
+        backward(Hq, Hr, pb_out, qb_out, ws_bwd)
 
     step()  # warm-up outside capture
     torch.cuda.synchronize()
@@ -86,8 +96,10 @@ def test_training_step_graph_replays_match_eager(io, N, D, T):
         # the same calls, eagerly, into fresh outputs
         h, Hp, Hq, Hr = mhc.mhc_pre(x, phi, bias, **kw)
         xn_e = mhc.mhc_post(x, y, Hq, Hr)
-        dx, dy, dHq, dHr = mhc.mhc_post_bwd(dxn, x, y, Hq, Hr)
-        _, dphi, dbias, dal = mhc.mhc_pre_bwd(dh, x, phi, bias, dHq, dHr, dx, **kw)
+        pb = tuple(torch.empty_like(t) for t in pb_out)
+        qb = tuple(torch.empty_like(t) for t in qb_out)
+        _, dphi, dbias, dal = backward(Hq, Hr, pb, qb, torch.empty_like(ws_bwd))
+        dx, dy, dHq, dHr = pb
         torch.cuda.synchronize()
         ref = (h, Hp, Hq, Hr, xn_e, dx, dy, dHq, dHr, dphi, dbias)
         names = ("h", "H_pre", "H_post", "H_res", "x_next", "dx", "dy", "dH_post", "dH_res", "dphi", "dbias")
