@@ -447,13 +447,14 @@ def main():
                                 "algo_bytes": ab[name], "gbps": gbps, "frac_of_peak": gbps / HBM_PEAK_GBPS,
                                 "kernels": call_kernels[name]}
 
-    # roofline: the single-kernel call that takes the most time in the step,
+    # roofline: the single-kernel call of the step that takes the most time,
     # so that its event time is one kernel's duration (the rocprofv3 summary
     # lists the same kernel); the multi-kernel hc_pre backward is reported
     # beside it as the largest call
-    single = [k for k in per_call if len(call_kernels[k]) == 1]
+    step_names = [name for name, _ in calls]
+    single = [k for k in step_names if len(call_kernels[k]) == 1]
     dom = max(single, key=lambda k: per_call[k]["avg_us"])
-    big = max(per_call, key=lambda k: per_call[k]["avg_us"])
+    big = max(step_names, key=lambda k: per_call[k]["avg_us"])
     src_hash = kernel_source_hash()
     traffic = load_traffic(dom, src_hash, args.workload)
     achieved = per_call[dom]["gbps"]
