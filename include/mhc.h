@@ -141,10 +141,9 @@ mhc_status mhc_pre_bwd(const mhc_desc* desc, const void* dh, const void* x, cons
  *   dx = Σ_n H_res[n,m]·dx_next[n] + (the hc_pre part written by mhc_pre_bwd)
  * (I/O dtype, overwritten).  For a block x → hc_pre → f → hc_post → x_next
  * this is the state gradient mhc_post_bwd + mhc_pre_bwd produce together,
- * with mhc_post_bwd called with dx = NULL; the H_res term is kept in fp32
- * until the final rounding (bf16, N = 4, D % 256 == 0) or rounded once as
- * mhc_post_bwd does (other shapes), so results agree with the two calls to
- * rounding.  dphi, dbias and dalpha are exactly those of mhc_pre_bwd.
+ * with mhc_post_bwd called with dx = NULL; the H_res term is rounded to the
+ * I/O dtype as mhc_post_bwd rounds its dx, so every output equals that of the
+ * two calls bit for bit.
  * dx_next and H_res are the arguments mhc_post_bwd took.  dx may be dx_next
  * itself (the gradient is then formed in place), but must not overlap it
  * otherwise, nor x or dh.  Same workspace as mhc_pre_bwd. */

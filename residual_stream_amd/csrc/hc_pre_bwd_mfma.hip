@@ -473,10 +473,10 @@ __global__ __launch_bounds__(kCoefThreads) void bwd_coef_kernel(
 // worked on (two register buffers; vector memory completes in order, so those
 // loads never wait on the stores issued after them).
 // MIX: the kernel reads dx_next and H_res instead of dx and writes
-// dx = H_resᵀ·dx_next + dx̄ − β·x + H_pre[n]·dh, the hc_post part formed in
-// fp32 (the four streams of a piece's token and d-chunk sit in lanes
-// pc + 16n of the same wave: lanes l ^ 16, l ^ 32, l ^ 48, reached with the
-// permlane swaps).
+// dx = H_resᵀ·dx_next + dx̄ − β·x + H_pre[n]·dh.  A thread's four pieces are
+// then the four streams of one token and d-chunk, so the mix needs no other
+// lane; it is rounded to bf16 exactly as mhc_post_bwd rounds its dx, which
+// makes the result that of mhc_post_bwd followed by mhc_pre_bwd, bit for bit.
 constexpr int kDxThreads = 256;
 constexpr int kDxWd = 128;        // d per stream per slice
 constexpr int kDxK = kN * kDxWd;  // 512 k per slice
@@ -489,18 +489,6 @@ constexpr int kHRow = kDxWd + 8;  // bf16 per dh row
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
-// v of lane l ^ 16 and of lane l ^ 32 (v_permlane16_swap / v_permlane32_swap
-// with both operands v: the first result keeps the even rows or the low half
-// and receives the partner's value in the others, the second the reverse).
-// Every lane of the wave must be active.
-__device__ __forceinline__ uint32_t lane_xor16(uint32_t v, bool even_row) {
-  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  return even_row ? r[1] : r[0];
-}
-__device__ __forceinline__ uint32_t lane_xor32(uint32_t v, bool low_half) {
-  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return low_half ? r[1] : r[0];
-}
 __device__ __forceinline__ f32x4_t mfma16(s16x4_t a, s16x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
@@ -552,12 +540,16 @@ __global__ __launch_bounds__(kDxThreads, 2) void bwd_dx_kernel(
 #pragma unroll
   for (int kb = 0; kb < 8; ++kb) dacc[kb][0] = dacc[kb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // This thread's pieces: token pt[j] = 4j + tid/64, stream pn, chunk pc.
+  // This thread's pieces j = 0..3, chunk pc: token 4j + tid/64 and stream pn,
+  // or (MIX) token tid/16 and stream j.  Either way a wave access covers four
+  // 256-byte runs.
   const int pn = (tid >> 4) & 3, pc = tid & 15;
+  auto ptok = [&](int j) { return MIX ? tid >> 4 : 4 * j + (tid >> 6); };
+  auto pstr = [&](int j) { return MIX ? j : pn; };
   uint32_t vo[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    vo[j] = (uint32_t)((((4 * j + (tid >> 6)) * (int64_t)K) + (int64_t)pn * D + d_base + 8 * pc) * 2);
+    vo[j] = (uint32_t)(((ptok(j) * (int64_t)K) + (int64_t)pstr(j) * D + d_base + 8 * pc) * 2);
   // its dh piece: token tid/16, chunk tid mod 16
   const int ht = tid >> 4;
   const uint32_t vh = (uint32_t)(((int64_t)ht * D + d_base + 8 * pc) * 2);
@@ -610,7 +602,7 @@ __global__ __launch_bounds__(kDxThreads, 2) void bwd_dx_kernel(
     // their loads read zeros)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<uint4*>(&xs[(4 * j + (tid >> 6)) * kXRow + pn * kDxWd + 8 * pc]) = bx[SL][j];
+      *reinterpret_cast<uint4*>(&xs[ptok(j) * kXRow + pstr(j) * kDxWd + 8 * pc]) = bx[SL][j];
     *reinterpret_cast<uint4*>(&hs[SL][ht * kHRow + 8 * pc]) = bh[SL];
     {
       const float4 v = bc[SL];
@@ -661,47 +653,55 @@ __global__ __launch_bounds__(kDxThreads, 2) void bwd_dx_kernel(
     // ---- finish this thread's pieces
     const uint32_t rows = rows_in(t0);
     const auto ro = make_rsrc(dx + (rows > 0 ? t0 : 0) * K, rows * (uint32_t)K * 2);
+    // MIX: the token's hc_post part, dx[m] = Σ_n H_res[n][m]·dx_next[n] in
+    // the arithmetic of mhc_post_bwd (fused multiply-adds over n from zero,
+    // rounded to bf16), for the four streams m this thread holds
+    uint4 mixed[4];
+    if constexpr (MIX) {
+      const int t = tid >> 4;
+      float hr[kN][kN];
+#pragma unroll
+      for (int n = 0; n < kN; ++n) {
+        const float4 r = *reinterpret_cast<const float4*>(&hrs[SL][t][n * kN]);
+        hr[n][0] = r.x;
+        hr[n][1] = r.y;
+        hr[n][2] = r.z;
+        hr[n][3] = r.w;
+      }
+#pragma unroll
+      for (int m = 0; m < kN; ++m) {
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+          for (int n = 0; n < kN; ++n) {
+            const uint32_t g = (&bd[SL][n].x)[q];
+            a0 += hr[n][m] * bf16_lo(g);
+            a1 += hr[n][m] * bf16_hi(g);
+          }
+          w[q] = pack_bf16x2(a0, a1);
+        }
+        mixed[m] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int t = 4 * j + (tid >> 6);
-      const float* rp = &dxr[t * kRRow + pn * kDxWd + 8 * pc];
+      const int t = ptok(j), sn = pstr(j);
+      const float* rp = &dxr[t * kRRow + sn * kDxWd + 8 * pc];
       const float4 r0 = *reinterpret_cast<const float4*>(rp);
       const float4 r1 = *reinterpret_cast<const float4*>(rp + 4);
       const uint4 hv = *reinterpret_cast<const uint4*>(&hs[SL][t * kHRow + 8 * pc]);
-      const float beta = bs[SL][t], hp = hps[SL][t][pn];
+      const float beta = bs[SL][t], hp = hps[SL][t][sn];
       const float rv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-      const uint4 xv = bx[SL][j], dv = bd[SL][j];
+      const uint4 xv = bx[SL][j], dv = MIX ? mixed[j] : bd[SL][j];
       const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, hw[4] = {hv.x, hv.y, hv.z, hv.w},
                      dw[4] = {dv.x, dv.y, dv.z, dv.w};
-      // the hc_post part of the piece: dx_next itself, or (MIX) column pn of
-      // H_res applied to the token's four streams
       float base[8];
-      if constexpr (MIX) {
-        // stream pn ^ k sits in lane l ^ 16k: sum over k = 0..3 (this lane's
-        // stream first), H_res[t][pn ^ k][pn]·dx_next[pn ^ k]
-        const bool even_row = (lane & 16) == 0, low_half = lane < 32;
-        float hk[kN];
 #pragma unroll
-        for (int k = 0; k < kN; ++k) hk[k] = hrs[SL][t][(pn ^ k) * kN + pn];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t w1 = lane_xor16(dw[q], even_row);
-          const uint32_t gk[kN] = {dw[q], w1, lane_xor32(dw[q], low_half), lane_xor32(w1, low_half)};
-          float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-          for (int k = 0; k < kN; ++k) {
-            a0 += hk[k] * bf16_lo(gk[k]);
-            a1 += hk[k] * bf16_hi(gk[k]);
-          }
-          base[2 * q] = a0;
-          base[2 * q + 1] = a1;
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          base[2 * q] = bf16_lo(dw[q]);
-          base[2 * q + 1] = bf16_hi(dw[q]);
-        }
+      for (int q = 0; q < 4; ++q) {
+        base[2 * q] = bf16_lo(dw[q]);
+        base[2 * q + 1] = bf16_hi(dw[q]);
       }
       uint32_t ow[4];
 #pragma unroll
