@@ -1,13 +1,14 @@
 // Drives the mHC C ABI from host code alone (no Python, no torch): reads the
 // inputs a test wrote, runs mhc_pre, mhc_post, mhc_post_bwd and mhc_pre_bwd on
-// its own device buffers and stream, checks a few argument errors, and writes
-// every output back for the test to compare with the Python binding's.
+// its own device buffers and stream, then the backward again as mhc_post_bwd
+// without dx + mhc_pre_bwd_mix, checks a few argument errors, and writes every
+// output back for the test to compare with the Python binding's.
 //
 // Input file (native byte order): int64 T; int32 N, D, io, iters; float eps,
 // alpha_pre, alpha_post, alpha_res; then x[T·N·D], y[T·D] (I/O dtype),
 // phi[N·D·C], bias[C] (fp32), dh[T·D], dx_next[T·N·D] (I/O dtype).
 // Output file: h, H_pre, H_post, H_res, x_next, dx, dy, dH_post, dH_res,
-// dphi, dbias, dalpha, in that order, raw.
+// dphi, dbias, dalpha, then the mixing pair's dx, in that order, raw.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -121,6 +122,15 @@ int main(int argc, char** argv) {
   mhc_ok(mhc_pre_bwd(&d, dh.d, x.d, (float*)phi.d, (float*)bias.d, (float*)dHq.d, (float*)dHr.d, dx.d,
                      (float*)dphi.d, (float*)dbias.d, (float*)dalpha.d, ws_bwd.d, wb, s),
          "mhc_pre_bwd");
+  // the same backward with hc_post's share of dx formed inside the hc_pre backward
+  Buf dx2(T * N * D * e), dy2(T * D * e), dHq2(T * N * 4), dHr2(T * N * N * 4), dphi2(N * D * C * 4),
+      dbias2(C * 4);
+  mhc_ok(mhc_post_bwd(&d, dxn.d, x.d, y.d, (float*)Hq.d, (float*)Hr.d, nullptr, dy2.d, (float*)dHq2.d,
+                      (float*)dHr2.d, s),
+         "mhc_post_bwd without dx");
+  mhc_ok(mhc_pre_bwd_mix(&d, dh.d, x.d, (float*)phi.d, (float*)bias.d, (float*)dHq2.d, (float*)dHr2.d, dxn.d,
+                         (float*)Hr.d, dx2.d, (float*)dphi2.d, (float*)dbias2.d, nullptr, ws_bwd.d, wb, s),
+         "mhc_pre_bwd_mix");
   hip_ok(hipStreamSynchronize(s), "hipStreamSynchronize");
   hip_ok(hipStreamDestroy(s), "hipStreamDestroy");
 
@@ -130,6 +140,7 @@ int main(int argc, char** argv) {
   Buf* da = &dalpha;
   da->n = 3 * 4;
   write_from(out, *da);
+  write_from(out, dx2);
   std::fclose(out);
   return 0;
 }

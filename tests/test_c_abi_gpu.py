@@ -1,7 +1,8 @@
 """The C ABI driven from host code alone: tests/c/mhc_abi_run.cpp (built by
 the package build) allocates its own device buffers and stream, runs the
-forward and backward calls on inputs this test writes, and must produce the
-same bits as the Python binding on the same inputs.  It also checks that
+forward and backward calls on inputs this test writes (the backward twice:
+mhc_post_bwd + mhc_pre_bwd, and mhc_post_bwd without dx + mhc_pre_bwd_mix),
+and must produce the same bits as the Python binding on the same inputs.  It also checks that
 argument errors are reported before anything runs."""
 
 from __future__ import annotations
@@ -57,9 +58,9 @@ def test_host_program_matches_binding(io, T, N, D, tmp_path):
     dx, dy, dHq, dHr = mhc.mhc_post_bwd(dev(inp.dx_next, io), x, y, Hq, Hr)
     dx, dphi, dbias, dalpha = mhc.mhc_pre_bwd(dev(inp.dh, io), x, phi, bias, dHq, dHr, dx, **kw)
     torch.cuda.synchronize()
-    ours = [h, Hp, Hq, Hr, xn, dx, dy, dHq, dHr, dphi, dbias, dalpha[:3]]
+    ours = [h, Hp, Hq, Hr, xn, dx, dy, dHq, dHr, dphi, dbias, dalpha[:3], dx]
     names = ["h", "H_pre", "H_post", "H_res", "x_next", "dx", "dy", "dH_post", "dH_res", "dphi", "dbias",
-             "dalpha"]
+             "dalpha", "dx of the mixing pair"]
     data = fout.read_bytes()
     off = 0
     for name, t in zip(names, ours):
