@@ -36,11 +36,11 @@ __global__ __launch_bounds__(kBwdThreads) void hc_post_bwd_generic(
   const int64_t xb = t * (int64_t)N * D;
   for (int d0 = threadIdx.x * 8; d0 < D; d0 += kBwdThreads * 8) {
     float g[N][8], xv[N][8], yv[8];
-    load8<IO>(y, t * D + d0, yv);
+    load8_stream<IO>(y, t * D + d0, yv);
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-      load8<IO>(dxn, xb + (int64_t)n * D + d0, g[n]);
-      load8<IO>(x, xb + (int64_t)n * D + d0, xv[n]);
+      load8_stream<IO>(dxn, xb + (int64_t)n * D + d0, g[n]);
+      load8_stream<IO>(x, xb + (int64_t)n * D + d0, xv[n]);
     }
     if constexpr (WDX) {
 #pragma unroll
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kBwdThreads) void hc_post_bwd_generic(
           for (int n = 0; n < N; ++n) a += hr[n][m] * g[n][j];
           o[j] = a;
         }
-        store8<IO>(dx, xb + (int64_t)m * D + d0, o);
+        store8_stream<IO>(dx, xb + (int64_t)m * D + d0, o);
       }
     }
     float o[8];
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kBwdThreads) void hc_post_bwd_generic(
       for (int n = 0; n < N; ++n) a += hp[n] * g[n][j];
       o[j] = a;
     }
-    store8<IO>(dy, t * D + d0, o);
+    store8_stream<IO>(dy, t * D + d0, o);
 #pragma unroll
     for (int n = 0; n < N; ++n) {
 #pragma unroll
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(kBwdThreads) void res_mix_t_kernel(const void* __re
   for (int d0 = threadIdx.x * 8; d0 < D; d0 += kBwdThreads * 8) {
     float g[N][8];
 #pragma unroll
-    for (int n = 0; n < N; ++n) load8<IO>(dxn, xb + (int64_t)n * D + d0, g[n]);
+    for (int n = 0; n < N; ++n) load8_stream<IO>(dxn, xb + (int64_t)n * D + d0, g[n]);
 #pragma unroll
     for (int m = 0; m < N; ++m) {
       float o[8];
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kBwdThreads) void res_mix_t_kernel(const void* __re
         for (int n = 0; n < N; ++n) a += hr[n][m] * g[n][j];
         o[j] = a;
       }
-      store8<IO>(dx, xb + (int64_t)m * D + d0, o);
+      store8_stream<IO>(dx, xb + (int64_t)m * D + d0, o);
     }
   }
 }

@@ -24,9 +24,9 @@ __global__ __launch_bounds__(kPostThreads) void hc_post_generic(
   const int64_t xb = t * (int64_t)N * D;
   for (int d0 = threadIdx.x * 8; d0 < D; d0 += kPostThreads * 8) {
     float xv[N][8], yv[8];
-    load8<IO>(y, t * D + d0, yv);
+    load8_stream<IO>(y, t * D + d0, yv);
 #pragma unroll
-    for (int m = 0; m < N; ++m) load8<IO>(x, xb + (int64_t)m * D + d0, xv[m]);
+    for (int m = 0; m < N; ++m) load8_stream<IO>(x, xb + (int64_t)m * D + d0, xv[m]);
 #pragma unroll
     for (int n = 0; n < N; ++n) {
       float o[8];
@@ -39,7 +39,7 @@ __global__ __launch_bounds__(kPostThreads) void hc_post_generic(
         for (int m = 0; m < N; ++m) a = __builtin_fmaf(hr[n][m], xv[m][j], a);
         o[j] = a;
       }
-      store8<IO>(x_next, xb + (int64_t)n * D + d0, o);
+      store8_stream<IO>(x_next, xb + (int64_t)n * D + d0, o);
     }
   }
 }
