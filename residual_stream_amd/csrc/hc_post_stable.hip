@@ -45,8 +45,10 @@ struct Pack8;
 template <>
 struct Pack8<kBF16> {
   uint4 w;
-  __device__ __forceinline__ void load(const void* b, int64_t i) {
-    w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(b) + i);
+  __device__ __forceinline__ void load(const void* b, int64_t i) {  // non-temporal: a stream
+    typedef unsigned u4 __attribute__((ext_vector_type(4)));
+    const u4 v = __builtin_nontemporal_load(reinterpret_cast<const u4*>(static_cast<const uint16_t*>(b) + i));
+    w = make_uint4(v.x, v.y, v.z, v.w);
   }
   __device__ __forceinline__ void zero() { w = make_uint4(0u, 0u, 0u, 0u); }
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff);
@@ -61,10 +63,12 @@ struct Pack8<kBF16> {
 template <>
 struct Pack8<kF32> {
   float4 a, b;
-  __device__ __forceinline__ void load(const void* p, int64_t i) {
-    const float4* q = reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
-    a = q[0];
-    b = q[1];
+  __device__ __forceinline__ void load(const void* p, int64_t i) {  // non-temporal: a stream
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    const f4* q = reinterpret_cast<const f4*>(static_cast<const float*>(p) + i);
+    const f4 u = __builtin_nontemporal_load(q), v = __builtin_nontemporal_load(q + 1);
+    a = make_float4(u.x, u.y, u.z, u.w);
+    b = make_float4(v.x, v.y, v.z, v.w);
   }
   __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff);
@@ -97,8 +101,13 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ Rsrc rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+// Cache policy: the norm weights are read for every token and keep the
+// default; the tensor streams (read or written once) go non-temporal, which
+// measured faster for the hc_post kernels on MI355X.
+constexpr int kStream = 2;  // nt
+template <int POLICY = 0>
 __device__ __forceinline__ uint4 bload16(Rsrc r, uint32_t voff, uint32_t soff) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, POLICY);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 // 16-byte store.  The scalar offset is always the literal 0 and any stream
@@ -106,8 +115,8 @@ __device__ __forceinline__ uint4 bload16(Rsrc r, uint32_t voff, uint32_t soff) {
 // leaves out the wait state that protects a wide store's data registers from
 // the next VALU write, and gfx950 then stores a corrupted first word on some
 // lanes.
-__device__ __forceinline__ void bstore16(Rsrc r, uint32_t voff, uint4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{v.x, v.y, v.z, v.w}, r, (int)voff, 0, 0);
+__device__ __forceinline__ void bstore16(Rsrc r, uint32_t voff, uint4 v) {  // streams only
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{v.x, v.y, v.z, v.w}, r, (int)voff, 0, kStream);
 }
 __device__ __forceinline__ void load_w8(Rsrc r, uint32_t voff, uint32_t soff, float v[8]) {
   const uint4 a = bload16(r, voff, soff), b = bload16(r, voff + 16, soff);
@@ -129,10 +138,10 @@ __device__ __forceinline__ void store8b(Rsrc r, uint32_t voff, uint32_t off, con
 }
 
 __device__ __forceinline__ void Pack8<kBF16>::load(Rsrc r, uint32_t voff, uint32_t soff) {
-  w = bload16(r, voff, soff);
+  w = bload16<kStream>(r, voff, soff);
 }
 __device__ __forceinline__ void Pack8<kF32>::load(Rsrc r, uint32_t voff, uint32_t soff) {
-  const uint4 p = bload16(r, voff, soff), q = bload16(r, voff + 16, soff);
+  const uint4 p = bload16<kStream>(r, voff, soff), q = bload16<kStream>(r, voff + 16, soff);
   a = make_float4(__uint_as_float(p.x), __uint_as_float(p.y), __uint_as_float(p.z), __uint_as_float(p.w));
   b = make_float4(__uint_as_float(q.x), __uint_as_float(q.y), __uint_as_float(q.z), __uint_as_float(q.w));
 }
@@ -240,7 +249,7 @@ __global__ __launch_bounds__(kMaxThreads) void post_stable_fwd(
   for (int j = 0; j < CPT; ++j) {
     if (!ok[j]) continue;
 #pragma unroll
-    for (int n = 0; n < N; ++n) store8<IO>(x_next, xb + (int64_t)n * D + d0[j], z[j][n]);
+    for (int n = 0; n < N; ++n) store8_stream<IO>(x_next, xb + (int64_t)n * D + d0[j], z[j][n]);
   }
 }
 
