@@ -119,11 +119,16 @@ class _Post(torch.autograd.Function):
     @staticmethod
     def backward(ctx, dx_next):
         x, y, H_post, H_res, y_weight, out_weight = ctx.saved_tensors
-        if y_weight is None and out_weight is None:
+        T, N, D = x.shape
+        if y_weight is None and out_weight is None and mhc.mix_fuses(N, D, mhc._io_of(x)):
             # dx is formed by the hc_pre backward of this block from dx_next
             dx_next = dx_next.contiguous()
             _, dy, dHq, dHr = mhc.mhc_post_bwd(dx_next, x, y, H_post, H_res, want_dx=False)
             ctx.handoff.mix = (dx_next, H_res)
+            dyw = dow = None
+        elif y_weight is None and out_weight is None:
+            dx, dy, dHq, dHr = mhc.mhc_post_bwd(dx_next.contiguous(), x, y, H_post, H_res)
+            ctx.handoff.dx = dx  # the hc_pre backward of this block adds to it
             dyw = dow = None
         else:
             dx, dy, dHq, dHr, dyw, dow = mhc.mhc_post_stable_bwd(
@@ -226,20 +231,24 @@ class _PostPre(torch.autograd.Function):
         # hc_pre backward of block l + 1: the next boundary (or the last
         # block's hc_post) handed over its dx_next and H_res, from which the
         # state gradient of x_{l+1} is formed here
-        mix = ctx.handoff_in.mix
-        ctx.handoff_in.mix = None
+        mix, dx_in = ctx.handoff_in.mix, ctx.handoff_in.dx
+        ctx.handoff_in.mix = ctx.handoff_in.dx = None
         if mix is not None:
             dx_next, dphi, dbias, dalpha = mhc.mhc_pre_bwd_mix(
                 dh.contiguous(), x_next, phi, bias, dHq.contiguous(), dHr.contiguous(), mix[0], mix[1], **kw)
         else:
             dx_next, dphi, dbias, dalpha = mhc.mhc_pre_bwd(
                 dh.contiguous(), x_next, phi, bias, dHq.contiguous(), dHr.contiguous(),
-                torch.zeros_like(x_next), **kw)
+                dx_in if dx_in is not None else torch.zeros_like(x_next), **kw)
         if dxn is not None:  # x_{l+1} also used outside the stack
             dx_next = dx_next + dxn
         # hc_post backward of block l, its dx left to the previous boundary
-        _, dy, dHq_in, dHr_in = mhc.mhc_post_bwd(dx_next, x, y, H_post_in, H_res_in, want_dx=False)
-        ctx.handoff_out.mix = (dx_next, H_res_in)
+        if mhc.mix_fuses(N, D, mhc._io_of(x)):
+            _, dy, dHq_in, dHr_in = mhc.mhc_post_bwd(dx_next, x, y, H_post_in, H_res_in, want_dx=False)
+            ctx.handoff_out.mix = (dx_next, H_res_in)
+        else:
+            dx, dy, dHq_in, dHr_in = mhc.mhc_post_bwd(dx_next, x, y, H_post_in, H_res_in)
+            ctx.handoff_out.dx = dx
         dalpha = dalpha.cpu() if want_dalpha else None
         return None, dy, dHq_in, dHr_in, dphi, dbias, dalpha, None, None, None, None
 

@@ -63,12 +63,10 @@ struct Pack8<kBF16> {
 template <>
 struct Pack8<kF32> {
   float4 a, b;
-  __device__ __forceinline__ void load(const void* p, int64_t i) {  // non-temporal: a stream
-    typedef float f4 __attribute__((ext_vector_type(4)));
-    const f4* q = reinterpret_cast<const f4*>(static_cast<const float*>(p) + i);
-    const f4 u = __builtin_nontemporal_load(q), v = __builtin_nontemporal_load(q + 1);
-    a = make_float4(u.x, u.y, u.z, u.w);
-    b = make_float4(v.x, v.y, v.z, v.w);
+  __device__ __forceinline__ void load(const void* p, int64_t i) {
+    const float4* q = reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+    a = q[0];
+    b = q[1];
   }
   __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff);
@@ -102,8 +100,9 @@ __device__ __forceinline__ Rsrc rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 // Cache policy: the norm weights are read for every token and keep the
-// default; the tensor streams (read or written once) go non-temporal, which
-// measured faster for the hc_post kernels on MI355X.
+// default; bf16 tensor streams (read or written once) go non-temporal, which
+// measured faster for the hc_post kernels on MI355X (fp32 streams keep the
+// default).
 constexpr int kStream = 2;  // nt
 template <int POLICY = 0>
 __device__ __forceinline__ uint4 bload16(Rsrc r, uint32_t voff, uint32_t soff) {
@@ -115,8 +114,9 @@ __device__ __forceinline__ uint4 bload16(Rsrc r, uint32_t voff, uint32_t soff) {
 // leaves out the wait state that protects a wide store's data registers from
 // the next VALU write, and gfx950 then stores a corrupted first word on some
 // lanes.
-__device__ __forceinline__ void bstore16(Rsrc r, uint32_t voff, uint4 v) {  // streams only
-  __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{v.x, v.y, v.z, v.w}, r, (int)voff, 0, kStream);
+template <int POLICY>
+__device__ __forceinline__ void bstore16(Rsrc r, uint32_t voff, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{v.x, v.y, v.z, v.w}, r, (int)voff, 0, POLICY);
 }
 __device__ __forceinline__ void load_w8(Rsrc r, uint32_t voff, uint32_t soff, float v[8]) {
   const uint4 a = bload16(r, voff, soff), b = bload16(r, voff + 16, soff);
@@ -129,10 +129,10 @@ template <int IO>
 __device__ __forceinline__ void store8b(Rsrc r, uint32_t voff, uint32_t off, const float v[8]) {
   voff += off;
   if constexpr (IO == kF32) {
-    bstore16(r, voff, make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])));
-    bstore16(r, voff + 16, make_uint4(__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])));
+    bstore16<0>(r, voff, make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])));
+    bstore16<0>(r, voff + 16, make_uint4(__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])));
   } else {
-    bstore16(r, voff, make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+    bstore16<kStream>(r, voff, make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
                                        pack_bf16x2(v[6], v[7])));
   }
 }
@@ -141,7 +141,7 @@ __device__ __forceinline__ void Pack8<kBF16>::load(Rsrc r, uint32_t voff, uint32
   w = bload16<kStream>(r, voff, soff);
 }
 __device__ __forceinline__ void Pack8<kF32>::load(Rsrc r, uint32_t voff, uint32_t soff) {
-  const uint4 p = bload16<kStream>(r, voff, soff), q = bload16<kStream>(r, voff + 16, soff);
+  const uint4 p = bload16(r, voff, soff), q = bload16(r, voff + 16, soff);
   a = make_float4(__uint_as_float(p.x), __uint_as_float(p.y), __uint_as_float(p.z), __uint_as_float(p.w));
   b = make_float4(__uint_as_float(q.x), __uint_as_float(q.y), __uint_as_float(q.z), __uint_as_float(q.w));
 }

@@ -73,10 +73,11 @@ __device__ __forceinline__ void store8(void* base, int64_t i, const float v[8]) 
   }
 }
 
-// load8 / store8 with the non-temporal hint (global_load/store … nt), for
-// the streaming hc_post kernels: measured on MI355X, the hint takes hc_post
-// from ≈75 to ≈65 µs and its backward from ≈112 to ≈101 µs (≈82 to ≈72 µs
-// without dx) at T = 4096, N = 4, D = 5120, bf16.  The split-K hc_pre and the
+// load8 / store8 with the non-temporal hint (global_load/store … nt) for bf16
+// streams, for the streaming hc_post kernels: measured on MI355X, the hint
+// takes hc_post from ≈75 to ≈65 µs and its backward from ≈112 to ≈101 µs
+// (≈82 to ≈72 µs without dx) at T = 4096, N = 4, D = 5120, bf16.  fp32
+// streams keep the default policy (the hint slowed the fp32 backward).  The split-K hc_pre and the
 // hc_pre backward passes keep the default policy: there the hint cost more
 // than it gained (the next call re-reads the same tensors while they are
 // still cached).
@@ -85,9 +86,7 @@ __device__ __forceinline__ void load8_stream(const void* base, int64_t i, float 
   typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
   const u32x4_t* p = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(base) + i * IoT<IO>::bytes);
   if constexpr (IO == kF32) {
-    const u32x4_t a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
-    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
-    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+    load8<IO>(base, i, v);
   } else {
     const u32x4_t w = __builtin_nontemporal_load(p);
     v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
@@ -102,10 +101,7 @@ __device__ __forceinline__ void store8_stream(void* base, int64_t i, const float
   typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
   u32x4_t* p = reinterpret_cast<u32x4_t*>(static_cast<char*>(base) + i * IoT<IO>::bytes);
   if constexpr (IO == kF32) {
-    __builtin_nontemporal_store(u32x4_t{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
-                                        __float_as_uint(v[3])}, p);
-    __builtin_nontemporal_store(u32x4_t{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]),
-                                        __float_as_uint(v[7])}, p + 1);
+    store8<IO>(base, i, v);
   } else {
     __builtin_nontemporal_store(u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
                                         pack_bf16x2(v[6], v[7])}, p);

@@ -253,6 +253,16 @@ def mhc_pre_bwd(dh, x, phi, bias, dH_post, dH_res, dx, *, iters=20, eps=1e-6,
     return dx, dphi, dbias, (dalpha[:3] if dalpha is not None else None)
 
 
+def mix_fuses(N: int, D: int, io: int, iters: int = 20) -> bool:
+    """True where mhc_pre_bwd_mix forms H_resᵀ·dx_next inside the hc_pre
+    backward's dx pass (bf16, N = 4, D a multiple of 256: the matrix-core
+    path), so that the pair mhc_post_bwd(want_dx=False) + mhc_pre_bwd_mix moves
+    a state-sized tensor less than mhc_post_bwd + mhc_pre_bwd.  Elsewhere the
+    library runs the mix as a kernel of its own first, and the two calls are
+    the faster choice (the results are the same bits either way)."""
+    return io == MHC_BF16 and N == 4 and D % 256 == 0 and iters <= 64
+
+
 def mhc_pre_bwd_mix(dh, x, phi, bias, dH_post, dH_res, dx_next, H_res, *, iters=20, eps=1e-6,
                     alphas=(0.01, 0.01, 0.01), want_dalpha=True, out=None, workspace=None, stream=None):
     """hc_pre backward with hc_post's share of the state gradient formed
