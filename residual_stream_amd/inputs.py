@@ -10,7 +10,9 @@ activations are drawn directly in float32, phi and bias in float64):
 * x[T,N,D] ~ N(0,1)        — the N-stream residual state
 * y[T,D] ~ N(0,1)          — the sublayer output
 * phi[N·D, N²+2N] ~ N(0, 1/(N·D))   (variance 1/(N·D), i.e. unit-variance raw logits)
-* bias[N²+2N] ~ N(0, 0.1)  (variance 0.1)
+* bias[N²+2N] ~ N(0, 0.1)  (variance 0.1; ``bias_std`` overrides the standard
+  deviation, e.g. 3 for logits large enough that one Sinkhorn round is far
+  from converged)
 * dh[T,D] ~ N(0,1), dx_next[T,N,D] ~ N(0,1)   — upstream gradients (optional)
 
 Inputs of the write-back calls that are not drawn above come from
@@ -95,7 +97,7 @@ class MhcInputs:
 
 def make_inputs(T: int, N: int, D: int, io: str = IO_F32, seed: int = 0,
                 alpha: float | tuple = 0.01, eps: float = 1e-6, iters: int = 20,
-                grads: bool = False) -> MhcInputs:
+                grads: bool = False, bias_std: float | None = None) -> MhcInputs:
     """Draw one seeded problem instance (see the module docstring for the recipe)."""
     rng = np.random.default_rng(seed)
     K = N * D
@@ -103,7 +105,8 @@ def make_inputs(T: int, N: int, D: int, io: str = IO_F32, seed: int = 0,
     x = to_io(rng.standard_normal((T, N, D), dtype=np.float32), io)
     y = to_io(rng.standard_normal((T, D), dtype=np.float32), io)
     phi = (rng.standard_normal((K, C)) * (1.0 / np.sqrt(K))).astype(np.float32)
-    bias = (rng.standard_normal(C) * np.sqrt(0.1)).astype(np.float32)
+    bstd = np.sqrt(0.1) if bias_std is None else float(bias_std)
+    bias = (rng.standard_normal(C) * bstd).astype(np.float32)
     dh = dxn = None
     if grads:
         dh = to_io(rng.standard_normal((T, D), dtype=np.float32), io)

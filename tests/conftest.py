@@ -11,3 +11,9 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built libmhc.so")
     config.addinivalue_line("markers", "slow: CPU test that takes more than a few seconds")
+
+
+def pytest_sessionfinish(session, exitstatus):
+    mod = sys.modules.get("mhc_testlib")
+    if mod is not None:
+        mod.write_stats()

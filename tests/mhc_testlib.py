@@ -1,7 +1,20 @@
 """Helpers shared by the GPU parity tests: move seeded inputs to the device,
-run the C-ABI path, run the oracle, compare normwise."""
+run the C-ABI path, run the oracle, compare normwise.
+
+The gate is normwise per output tensor, max|gpu - oracle| / max|oracle|.
+Beside it every comparison records elementwise statistics (reported, not
+gated): the largest absolute error, and the largest and 99th-percentile
+relative error over the elements whose reference magnitude is at least 1e-3
+of the tensor's largest (relative error is meaningless near zeros).  They are
+printed with the test's output and, when the environment variable
+MHC_PARITY_STATS names a file, written there as JSON lines at the end of the
+session.
+"""
 
 from __future__ import annotations
+
+import os
+import sys
 
 import numpy as np
 import torch
@@ -40,11 +53,42 @@ def normwise(got, ref) -> float:
     return float(num / den)
 
 
-def assert_close(name, got, ref, tol):
+STATS: list = []  # elementwise statistics of every comparison of this session
+
+
+def elementwise_stats(got, ref) -> dict:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    diff = np.abs(got - ref)
+    big = np.max(np.abs(ref)) if ref.size else 0.0
+    mask = np.abs(ref) >= 1e-3 * big if big > 0 else np.zeros(ref.shape, bool)
+    rel = diff[mask] / np.abs(ref[mask]) if mask.any() else np.zeros(1)
+    return {"max_abs": float(diff.max()) if diff.size else 0.0,
+            "max_rel": float(rel.max()), "p99_rel": float(np.percentile(rel, 99)),
+            "n": int(ref.size)}
+
+
+def assert_close(name, got, ref, tol, case: str = ""):
     err = normwise(got, ref)
+    st = elementwise_stats(got, ref)
+    st.update(name=name, case=case, normwise=err, tol=tol)
+    STATS.append(st)
+    print(f"    {name}: normwise {err:.2e} (gate {tol:.0e}); elementwise max abs {st['max_abs']:.2e}, "
+          f"max rel {st['max_rel']:.2e}, p99 rel {st['p99_rel']:.2e} over {st['n']}", flush=True)
+    sys.stdout.flush()
     assert np.all(np.isfinite(got)), f"{name}: non-finite output"
     assert err <= tol, f"{name}: normwise error {err:.3e} > {tol:.1e}"
     return err
+
+
+def write_stats():
+    path = os.environ.get("MHC_PARITY_STATS")
+    if not path or not STATS:
+        return
+    import json
+    with open(path, "a") as f:
+        for st in STATS:
+            f.write(json.dumps(st) + "\n")
 
 
 def gpu_forward(inp: MhcInputs, stream=None):

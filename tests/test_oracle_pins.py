@@ -279,3 +279,21 @@ def test_hc_pre_h_matches_explicit_loop():
         for d in range(8):
             ref = math.fsum(out["H_pre"][t, n] * x[t, n, d] for n in range(4))
             assert out["h"][t, d] == pytest.approx(ref, rel=1e-14, abs=1e-15)
+
+
+@pytest.mark.parametrize("iters", [1, 3])
+def test_large_logit_inputs_separate_round_counts(iters):
+    # The GPU tests of the Sinkhorn round count use bias std 3 at alpha = 1:
+    # there one or three rounds differ from twenty, and from the same number of
+    # column-first rounds, by far more than the bf16 gate (2e-2), so a wrong
+    # count or order fails them.
+    inp = make_inputs(64, 4, 256, io="bf16", seed=11, alpha=1.0, iters=iters, bias_std=3.0)
+    _, _, q = O.project(inp.x, inp.phi, inp.eps)
+    _, _, l_res = O.split_logits(q, inp.bias, inp.alphas, 4)
+    M0 = np.exp(l_res)
+    few = O.sinkhorn(M0, iters)
+    ref = O.sinkhorn(M0, 20)
+    col_first = np.swapaxes(O.sinkhorn(np.swapaxes(M0, -1, -2), iters), -1, -2)
+    assert np.max(np.abs(few - ref)) / np.max(np.abs(ref)) > 0.1
+    assert np.max(np.abs(few - col_first)) / np.max(np.abs(few)) > 0.1
+    np.testing.assert_array_equal(few, O.hc_pre(inp.x, inp.phi, inp.bias, inp.alphas, inp.eps, iters)["H_res"])

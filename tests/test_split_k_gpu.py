@@ -1,0 +1,178 @@
+"""The split-K hc_pre and the tiled hc_pre backward against the fp64 oracle,
+where their own structure can go wrong.
+
+The split-K forward (bf16, N = 4, D = 5120 or 2560) cuts each token's
+reduction into S = D/320 slices; a group of S workgroups walks the tiles
+grp, grp + Q, grp + 2Q, ... (16 tokens each, Q = compute units / S), keeps
+x in a ring of register buffers until the token's H_pre is known, and runs
+the gates and Sinkhorn of the tokens a workgroup finishes in batches that
+span 16/(16/S) of the group's tiles.  A token's coefficients sent to the wrong
+token, a ring slot taken out of turn, or a batch written to the wrong rows
+only shows where the projection matters: at alpha = 1 (at the workloads'
+alpha = 0.01 the logits are almost the bias, the same for every token).  So
+these cases run at alpha = 1, at full size, with sampled tokens that cover a
+whole tile at both ends of a group and every token of one workgroup's
+Sinkhorn batches, on both sides of a ragged end.
+
+The Sinkhorn round count and order (openPangu 2.0 analysis, §5.3: rows then
+columns, 20 rounds in the model) are pinned with large logits (bias standard
+deviation 3), where one or three rounds are far from converged, so that a
+wrong count or a column-first round moves H_res by much more than the gate.
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import mhc_oracle as O
+from residual_stream_amd import mhc
+from residual_stream_amd.inputs import make_coefficients, make_inputs, to_io
+
+from mhc_testlib import (TOL, assert_close, dev, gpu_backward, gpu_forward, host,
+                         oracle_backward, oracle_forward)
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+FWD_KEYS = ("h", "H_pre", "H_post", "H_res", "x_next")
+BWD_KEYS = ("dx", "dy", "dH_post", "dH_res", "dphi", "dbias", "dalpha")
+TILE = 16
+SLICE_D = 320
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _cus():
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def split_k_tokens(T, D, grp=3, slice_=5, extra=24, seed=0):
+    """Tokens that exercise the split-K kernel's structure: all tokens of the
+    first and the last tile of group `grp`, every token workgroup (grp,
+    slice_) finishes (its Sinkhorn batches), the last two tokens and a random
+    handful."""
+    S = D // SLICE_D
+    Q = _cus() // S
+    share = TILE // S
+    ntiles = (T + TILE - 1) // TILE
+    grp = min(grp, Q - 1, ntiles - 1)
+    slice_ = slice_ % S
+    nloc = (ntiles - grp + Q - 1) // Q
+    toks = set()
+    for tile in (grp, grp + (nloc - 1) * Q):
+        toks.update(range(tile * TILE, min(T, tile * TILE + TILE)))
+    for p in range(nloc):
+        for u in range(share):
+            toks.add((grp + p * Q) * TILE + slice_ * share + u)
+    toks.update((0, T - 2, T - 1))
+    rng = np.random.default_rng(seed)
+    toks.update(rng.choice(T, extra, replace=False).tolist())
+    return np.array(sorted(t for t in toks if 0 <= t < T))
+
+
+def check_forward(inp, tokens=None, tag=""):
+    _say(f"[fwd] {tag} T={inp.T} N={inp.N} D={inp.D} io={inp.io} alpha={inp.alphas[0]} "
+         f"iters={inp.iters} tokens={'all' if tokens is None else len(tokens)}")
+    g = gpu_forward(inp)
+    torch.cuda.synchronize()
+    r = oracle_forward(inp, tokens)
+    for k in FWD_KEYS:
+        got = host(g[k])
+        if tokens is not None:
+            got = got[tokens]
+        assert_close(k, got, r[k], TOL[inp.io], case=f"{tag} T={inp.T} D={inp.D}")
+
+
+# -------------------------------------------- split-K forward, alpha = 1 ---
+
+@pytest.mark.parametrize("T,D", [(4096, 5120), (4093, 5120), (2048, 2560), (4096, 2560), (4093, 2560)])
+def test_split_k_forward_alpha1_full_size(T, D):
+    inp = make_inputs(T, 4, D, io="bf16", seed=T + D, alpha=1.0)
+    check_forward(inp, tokens=split_k_tokens(T, D, seed=T), tag="split-K alpha=1")
+
+
+def test_split_k_forward_alpha1_other_group():
+    # the last group and slice, so that the sampled batch is not one position only
+    inp = make_inputs(4096, 4, 5120, io="bf16", seed=77, alpha=1.0)
+    check_forward(inp, tokens=split_k_tokens(4096, 5120, grp=10_000, slice_=15, seed=1),
+                  tag="split-K alpha=1, last group")
+
+
+@pytest.mark.parametrize("iters", [1, 3, 64])
+@pytest.mark.parametrize("T,D", [(17, 5120), (300, 5120), (300, 2560)])
+def test_split_k_sinkhorn_rounds(iters, T, D):
+    inp = make_inputs(T, 4, D, io="bf16", seed=iters + T + D, alpha=1.0, iters=iters, bias_std=3.0)
+    check_forward(inp, tag=f"split-K rounds={iters}")
+
+
+# --------------------------------- fused hc_post + next hc_pre, alpha = 1 ---
+
+@pytest.mark.parametrize("T,D", [(4096, 5120), (4093, 2560)])
+def test_fused_post_pre_alpha1_full_size(T, D):
+    _say(f"[post_pre] oracle composition, alpha=1, T={T} D={D}")
+    a = make_inputs(T, 4, D, io="bf16", seed=T + 5, alpha=1.0)
+    b = make_inputs(T, 4, D, io="bf16", seed=T + 1005, alpha=1.0)
+    Hq_ref, Hr_ref = make_coefficients(T, 4, seed=T + 2005)
+    x, y = dev(a.x, "bf16"), dev(a.y, "bf16")
+    kw = dict(iters=b.iters, eps=b.eps, alphas=b.alphas)
+    xn, h, Hp, Hq, Hr = mhc.mhc_post_pre(x, y, dev(Hq_ref), dev(Hr_ref), dev(b.phi), dev(b.bias), **kw)
+    torch.cuda.synchronize()
+    tk = split_k_tokens(T, D, seed=T + 5)
+    ref_xn = O.hc_post(a.x[tk], a.y[tk], Hq_ref[tk], Hr_ref[tk])
+    case = f"post_pre alpha=1 T={T} D={D}"
+    assert_close("x_next", host(xn)[tk], ref_xn, TOL["bf16"], case=case)
+    # the next layer reads the state as stored (rounded to bf16)
+    xn_io = to_io(ref_xn.astype(np.float32), "bf16").astype(np.float64)
+    ref = O.hc_pre(xn_io, b.phi, b.bias, b.alphas, b.eps, b.iters)
+    for name, got in (("h", h), ("H_pre", Hp), ("H_post", Hq), ("H_res", Hr)):
+        assert_close(name, host(got)[tk], ref[name], TOL["bf16"], case=case)
+
+
+# ----------------------------------------- tiled backward, alpha = 1 ---
+
+def _bwd_tokens(T, seed=0):
+    # both sides of every 16-token tile edge at the start and the end, and of
+    # the token splits' edges (multiples of 16 near T/12·k), plus random ones
+    rng = np.random.default_rng(seed)
+    toks = set(range(0, 33)) | set(range(T - 33, T))
+    for k in range(1, 12):
+        c = (T * k // 12) // TILE * TILE
+        toks.update((c - 1, c, c + 1))
+    toks.update(rng.choice(T, 40, replace=False).tolist())
+    return np.array(sorted(t for t in toks if 0 <= t < T))
+
+
+def check_backward(inp, tokens=None, tag=""):
+    _say(f"[bwd] {tag} T={inp.T} N={inp.N} D={inp.D} io={inp.io} alpha={inp.alphas[0]} iters={inp.iters}")
+    g = gpu_backward(inp)
+    torch.cuda.synchronize()
+    r = oracle_backward(inp)
+    for k in BWD_KEYS:
+        got, ref = host(g[k]), r[k]
+        if tokens is not None and k not in ("dphi", "dbias", "dalpha"):
+            got, ref = got[tokens], ref[tokens]
+        assert_close(k, got, ref, TOL[inp.io], case=f"{tag} T={inp.T} D={inp.D}")
+
+
+def test_tiled_backward_alpha1_full_size_bf16():
+    # B=1, S=4096, N=4, D=5120, bf16 I/O at alpha = 1: dx, dy, dH_* on sampled
+    # tokens, the whole dphi, dbias and dalpha against the full fp64 oracle
+    inp = make_inputs(4096, 4, 5120, io="bf16", seed=3, alpha=1.0, grads=True)
+    check_backward(inp, tokens=_bwd_tokens(4096), tag="tiled bwd alpha=1")
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("iters", [1, 3, 64])
+@pytest.mark.parametrize("T,D", [(70, 256), (37, 2560)])
+def test_tiled_backward_sinkhorn_rounds(io, iters, T, D):
+    inp = make_inputs(T, 4, D, io=io, seed=iters * 7 + T, alpha=1.0, iters=iters, bias_std=3.0, grads=True)
+    check_backward(inp, tag=f"tiled bwd rounds={iters}")
