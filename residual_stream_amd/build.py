@@ -21,8 +21,8 @@ ABI_RUN_SRC = os.path.join(os.path.dirname(HERE), "tests", "c", "mhc_abi_run.cpp
 ABI_RUN = os.path.join(os.path.dirname(HERE), "tests", "c", "_build", "mhc_abi_run")
 
 SOURCES = ["mhc_api.cpp", "hc_pre.hip", "hc_pre_mfma.hip", "hc_post.hip", "hc_bwd.hip",
-           "hc_pre_bwd_mfma.hip", "hc_pre_coop.hip", "hc_pre_decode.hip",
-           "hc_post_stable.hip"]
+           "hc_pre_bwd_mfma.hip", "hc_pre_decode.hip",
+           "hc_post_stable.hip", "hc_pre_tile.hip"]
 
 ARCH = "gfx950"
 # Packed-fp32 VALU instructions are switched off for every device pass.

@@ -177,7 +177,7 @@ bool pre_decode_eligible(const mhc_desc& d) {
   // few tokens (fewer still where the split-K kernel applies: it overtakes
   // this path between 16 and 32 tokens), and a partial-sum workspace of at
   // most a few MB
-  const int64_t max_t = pre_coop_eligible(d) ? 16 : kDecodeMaxT;
+  const int64_t max_t = pre_tile_eligible(d) ? 16 : kDecodeMaxT;
   return d.T <= max_t && (int64_t)d.N * d.D <= (1 << 20);
 }
 

@@ -470,13 +470,13 @@ static size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 size_t pre_workspace_bytes(const mhc_desc& d) {
   if (pre_decode_eligible(d)) return pre_decode_workspace_bytes(d);
+  if (pre_tile_eligible(d)) return pre_tile_workspace_bytes(d);
   const PreConfig pc = pick_pre(d);
   if (pc.tm == 0) return 0;
-  const size_t own = align256((size_t)pc.nsteps * pc.cg * pc.ps * 64 * sizeof(uint4));
-  // the cooperative kernel may take the call instead; room for either
-  const size_t coop = pre_coop_eligible(d) ? pre_coop_workspace_bytes(d) : 0;
-  return own > coop ? own : coop;
+  return align256((size_t)pc.nsteps * pc.cg * pc.ps * 64 * sizeof(uint4));
 }
+
+size_t post_pre_workspace_bytes(const mhc_desc& d) { return pre_workspace_bytes(d); }
 
 hipError_t launch_pre_generic(const mhc_desc& d, const void* x, const float* phi,
                               const float* bias, void* h, float* H_pre, float* H_post,
@@ -507,12 +507,8 @@ hipError_t launch_pre(const mhc_desc& d, const void* x, const float* phi, const 
                       hipStream_t s) {
   if (pre_decode_eligible(d)) return launch_pre_decode(d, x, phi, bias, h, H_pre, H_post, H_res, ws, s);
   const PreConfig pc = pick_pre(d);
+  if (pre_tile_eligible(d)) return launch_pre_tile(d, x, phi, bias, h, H_pre, H_post, H_res, ws, s);
   if (pc.tm == 0) return launch_pre_generic(d, x, phi, bias, h, H_pre, H_post, H_res, s);
-  if (pre_coop_eligible(d)) {
-    if (launch_pre_coop(d, x, phi, bias, h, H_pre, H_post, H_res, ws, s) == hipSuccess)
-      return hipSuccess;
-    (void)hipGetLastError();  // launch refused: clear the error and take the per-tile kernel
-  }
   if (d.io == kBF16) {
     if (pc.tm == 16) return launch_mfma<kBF16, 16, 10>(d, pc, x, phi, bias, h, H_pre, H_post, H_res, ws, s);
     return launch_mfma<kBF16, 8, 20>(d, pc, x, phi, bias, h, H_pre, H_post, H_res, ws, s);
@@ -524,12 +520,6 @@ hipError_t launch_pre(const mhc_desc& d, const void* x, const float* phi, const 
 hipError_t launch_post_pre(const mhc_desc& d, const void* x, const void* y, const float* H_post_in,
                            const float* H_res_in, void* x_next, const float* phi, const float* bias,
                            void* h, float* H_pre, float* H_post, float* H_res, void* ws, hipStream_t s) {
-  if (pre_coop_eligible(d) && pick_pre(d).tm != 0 && !pre_decode_eligible(d)) {
-    if (launch_post_pre_coop(d, x, y, H_post_in, H_res_in, x_next, phi, bias, h, H_pre, H_post, H_res,
-                             ws, s) == hipSuccess)
-      return hipSuccess;
-    (void)hipGetLastError();  // launch refused: clear the error and take the two kernels
-  }
   const hipError_t e = launch_post(d, x, y, H_post_in, H_res_in, x_next, s);
   if (e != hipSuccess) return e;
   return launch_pre(d, x_next, phi, bias, h, H_pre, H_post, H_res, ws, s);

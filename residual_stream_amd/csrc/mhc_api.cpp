@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <chrono>
 #include <cmath>
 #include <limits>
 
@@ -25,6 +26,15 @@ int device_cu_count() {
     n = 256;
   if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
   return n;
+}
+
+// Tags of the exchange records of the split-K kernels: one per call, not
+// repeated for 2^31 calls in a process; the top bit is set so that zeroed
+// memory never matches.
+uint32_t next_call_tag() {
+  static std::atomic<uint32_t> counter{
+      (uint32_t)((uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761u)};
+  return counter.fetch_add(1, std::memory_order_relaxed) | 0x80000000u;
 }
 
 }  // namespace mhc
@@ -190,7 +200,7 @@ mhc_status mhc_pre_bwd_mix(const mhc_desc* d, const void* dh, const void* x, con
 
 size_t mhc_post_pre_workspace_bytes(const mhc_desc* d) {
   if (check_desc(d) != MHC_OK) return 0;
-  return mhc::pre_workspace_bytes(*d);
+  return mhc::post_pre_workspace_bytes(*d);
 }
 
 mhc_status mhc_post_pre(const mhc_desc* d, const void* x, const void* y, const float* H_post_in,
@@ -211,7 +221,7 @@ mhc_status mhc_post_pre(const mhc_desc* d, const void* x, const void* y, const f
       overlaps(H_res, cr, H_res_in, cr) || overlaps(H_pre, cq, H_post_in, cq) ||
       overlaps(H_pre, cq, H_res_in, cr))
     return MHC_ERR_INVALID_ARG;
-  if (!workspace_ok(workspace, workspace_bytes, mhc::pre_workspace_bytes(*d)))
+  if (!workspace_ok(workspace, workspace_bytes, mhc::post_pre_workspace_bytes(*d)))
     return MHC_ERR_INVALID_ARG;
   return from_hip(mhc::launch_post_pre(*d, x, y, H_post_in, H_res_in, x_next, phi, bias, h, H_pre,
                                        H_post, H_res, workspace, stream));

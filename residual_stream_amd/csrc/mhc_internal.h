@@ -13,7 +13,19 @@ namespace mhc {
 // not mutable state).
 int device_cu_count();
 
+// A fresh tag for the exchange records of one split-K call (top bit set).
+uint32_t next_call_tag();
+
+// hc_pre with whole token tiles held on chip, the reduction split over groups
+// of four workgroups (bf16, N = 4, D = 5120 or 2560); φ packed into the
+// workspace as bf16 high and low parts first.
+bool pre_tile_eligible(const mhc_desc& d);
+size_t pre_tile_workspace_bytes(const mhc_desc& d);
+hipError_t launch_pre_tile(const mhc_desc& d, const void* x, const float* phi, const float* bias, void* h,
+                           float* H_pre, float* H_post, float* H_res, void* ws, hipStream_t s);
+
 size_t pre_workspace_bytes(const mhc_desc& d);
+size_t post_pre_workspace_bytes(const mhc_desc& d);
 hipError_t launch_pre(const mhc_desc& d, const void* x, const float* phi, const float* bias,
                       void* h, float* H_pre, float* H_post, float* H_res, void* ws,
                       hipStream_t s);
