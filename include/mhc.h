@@ -32,7 +32,8 @@
  *   - Alignment: every pointer 16-byte aligned.
  *   - Work is enqueued on `stream` and runs asynchronously; the library never
  *     allocates, frees or synchronises.  Its only global state is an atomic
- *     per-call counter (calls are thread-safe).  A workspace must not be in
+ *     per-call counter (calls are thread-safe), besides the per-thread switch
+ *     of mhc_trace_kernel_events.  A workspace must not be in
  *     use by two calls at once.  Outputs are overwritten, except `dx` of mhc_pre_bwd,
  *     which is read-modify-write.
  *   - Errors: argument checks are synchronous and return a status without
@@ -55,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MHC_ABI_VERSION 3
+#define MHC_ABI_VERSION 4
 
 typedef enum mhc_dtype { MHC_F32 = 0, MHC_BF16 = 1 } mhc_dtype;
 
@@ -69,7 +70,12 @@ typedef enum mhc_status {
 /* Problem descriptor.  T = tokens (batch × sequence), N streams, D hidden size
  * (multiple of 8), io = mhc_dtype, sinkhorn_iters ≥ 1 (≤ 64 for mhc_pre_bwd),
  * eps ≥ 0 inside the RMS square root, alpha_* the per-group gate scalars
- * multiplying the normalised projection before the bias is added. */
+ * multiplying the normalised projection before the bias is added.  `alpha`,
+ * if non-NULL, is a device pointer to the three gate scalars (pre, post, res;
+ * fp32, 4-byte aligned) that the kernels read instead of alpha_*: a trained α
+ * then stays on the device (no host round trip per step, and a captured graph
+ * follows its updates).  Leave it NULL (zero-initialise the struct) to use
+ * the scalars. */
 typedef struct mhc_desc {
   int64_t T;
   int32_t N;
@@ -80,6 +86,7 @@ typedef struct mhc_desc {
   float alpha_pre;
   float alpha_post;
   float alpha_res;
+  const float* alpha;
 } mhc_desc;
 
 /* Bytes of device workspace mhc_pre needs (0 if none).  Never fails; returns 0
@@ -90,16 +97,17 @@ size_t mhc_pre_workspace_bytes(const mhc_desc* desc);
  * coefficients H_pre, H_post, H_res.  `workspace` (may be NULL when
  * mhc_pre_workspace_bytes is 0) is scratch owned by the caller, at least
  * that many bytes, 256-byte aligned; its contents on entry are ignored.  For
- * bf16, N = 4, D = 5120 or 2560 the call splits each token's reduction across
+ * bf16, N = 4, D = 5120 or 2560 the call first packs φ into the workspace (as
+ * bf16 high and low parts, so the projection keeps fp32 accuracy on the
+ * matrix cores) and then splits each token's reduction across a group of
  * workgroups that exchange partial sums through the workspace, tagged per
  * call, so two calls that share a workspace must not overlap in time (on one
  * stream they never do).  Those workgroups wait for each other with bounded
  * waits; should one never arrive (e.g. far too few free compute units), the
  * affected tokens get NaN in h and in the coefficients rather than a hang or
- * silently wrong values.  The tag is drawn on the host when the call is made:
- * a HIP graph that replays a captured split-K call reuses it, so each replay
- * must find the workspace cleared (zero-filled by a kernel recorded in the same
- * graph before the call; zero never matches a tag). */
+ * silently wrong values.  The tag is a number each call takes from a
+ * device-wide counter, so the call can be captured in a HIP graph with any
+ * workspace, never cleared: every replay tags its records afresh. */
 mhc_status mhc_pre(const mhc_desc* desc, const void* x, const float* phi, const float* bias,
                    void* h, float* H_pre, float* H_post, float* H_res,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
@@ -159,16 +167,15 @@ const char* mhc_status_string(mhc_status status);
  * the same descriptor). */
 size_t mhc_post_pre_workspace_bytes(const mhc_desc* desc);
 
-/* hc_post of one layer fused with hc_pre of the next layer (openPangu 2.0
- * analysis §11.3: the write-back, the next RMSNorm and H_pre in one pass).
- * Computes x_next = H_res_in·x + H_post_in ⊗ y ([T][N][D], I/O dtype; the
- * mhc_post contract) and then, on x_next as stored, hc_pre of the next layer
- * with its phi, bias and the descriptor's Sinkhorn rounds, eps and gate
- * scalars: h, H_pre, H_post, H_res (the mhc_pre contract).  The results equal
- * mhc_post followed by mhc_pre bit for bit; for bf16, N = 4, D = 5120 or 2560
- * x_next is not read back (one pass over x and y instead of a write and a
- * re-read of x_next).  Outputs must not alias inputs; the workspace rules of
- * mhc_pre apply. */
+/* hc_post of one layer followed by hc_pre of the next layer (openPangu 2.0
+ * analysis §11.3 fuses the write-back, the next RMSNorm and H_pre).  Computes
+ * x_next = H_res_in·x + H_post_in ⊗ y ([T][N][D], I/O dtype; the mhc_post
+ * contract) and then, on x_next as stored, hc_pre of the next layer with its
+ * phi, bias and the descriptor's Sinkhorn rounds, eps and gate scalars: h,
+ * H_pre, H_post, H_res (the mhc_pre contract).  The results equal mhc_post
+ * followed by mhc_pre bit for bit (the call runs the two kernels; a single
+ * pass that keeps x_next on chip measured slower than the pair).  Outputs must
+ * not alias inputs; the workspace rules of mhc_pre apply. */
 mhc_status mhc_post_pre(const mhc_desc* desc, const void* x, const void* y, const float* H_post_in,
                         const float* H_res_in, const float* phi, const float* bias, void* x_next,
                         void* h, float* H_pre, float* H_post, float* H_res, void* workspace,
@@ -211,6 +218,21 @@ mhc_status mhc_post_stable_bwd(const mhc_desc* desc, const void* dx_next, const 
 
 /* MHC_ABI_VERSION of the built library. */
 int mhc_abi_version(void);
+
+/* Kernel-level timing, for benchmarks and profiling (off by default; not part
+ * of the method).  While `events` is non-NULL, every mhc_* call made on the
+ * calling host thread records events[2k] on its stream immediately before its
+ * k-th kernel launch and events[2k + 1] immediately after it, for k counted
+ * from this call up to `capacity` launches (later launches are not recorded);
+ * names[k] (if `names` is non-NULL) is set to a static string naming the
+ * kernel, and *count (if non-NULL) to the number of launches recorded so far.
+ * The events are the caller's (created with hipEventCreate, with timing) and
+ * must outlive the tracing; hipEventElapsedTime(events[2k], events[2k + 1])
+ * is then the k-th kernel's time on the device.  Calling it again restarts
+ * the count; mhc_trace_kernel_events(NULL, NULL, 0, NULL) stops.  The state is
+ * per host thread.  MHC_ERR_INVALID_ARG for a negative capacity, or a zero
+ * one with events. */
+mhc_status mhc_trace_kernel_events(hipEvent_t* events, const char** names, int capacity, int* count);
 
 #ifdef __cplusplus
 }

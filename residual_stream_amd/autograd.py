@@ -67,18 +67,18 @@ class _DxHandoff:
 class _Pre(torch.autograd.Function):
     @staticmethod
     def forward(ctx, x, phi, bias, alpha, iters, eps, handoff):
-        alphas = tuple(float(a) for a in alpha.tolist())  # alpha lives on the host
-        h, Hp, Hq, Hr = mhc.mhc_pre(x, phi, bias, iters=iters, eps=eps, alphas=alphas)
-        ctx.save_for_backward(x, phi, bias)
-        ctx.cfg = (iters, eps, alphas, alpha.requires_grad)
+        # alpha is a GPU tensor the kernels read on the device: no host round trip
+        h, Hp, Hq, Hr = mhc.mhc_pre(x, phi, bias, iters=iters, eps=eps, alphas=alpha)
+        ctx.save_for_backward(x, phi, bias, alpha)
+        ctx.cfg = (iters, eps, alpha.requires_grad)
         ctx.handoff = handoff
         ctx.mark_non_differentiable(Hp)  # used only inside the collapse
         return h, Hp, Hq, Hr
 
     @staticmethod
     def backward(ctx, dh, _dHp, dHq, dHr):
-        x, phi, bias = ctx.saved_tensors
-        iters, eps, alphas, want_dalpha = ctx.cfg
+        x, phi, bias, alphas = ctx.saved_tensors
+        iters, eps, want_dalpha = ctx.cfg
         T, N, D = x.shape
         dx, mix = ctx.handoff.dx, ctx.handoff.mix
         ctx.handoff.dx = ctx.handoff.mix = None
@@ -99,8 +99,7 @@ class _Pre(torch.autograd.Function):
             dx, dphi, dbias, dalpha = mhc.mhc_pre_bwd(
                 dh.contiguous(), x, phi, bias, dHq.contiguous(), dHr.contiguous(), dx,
                 iters=iters, eps=eps, alphas=alphas, want_dalpha=want_dalpha)
-        dalpha = dalpha.cpu() if want_dalpha else None
-        return dx, dphi, dbias, dalpha, None, None, None
+        return dx, dphi, dbias, (dalpha if want_dalpha else None), None, None, None
 
 
 class _Post(torch.autograd.Function):
@@ -143,8 +142,9 @@ class MHCBlock(torch.nn.Module):
     y[T, D] in the I/O dtype).
 
     Parameters: φ[N·D, N²+2N] and b[N²+2N] (fp32, on the GPU) and the three gate
-    scalars α = (α_pre, α_post, α_res) as a host tensor (their values are
-    launch parameters; their gradient comes back from the GPU); with the
+    scalars α = (α_pre, α_post, α_res), also a GPU tensor that the kernels
+    read on the device (so neither the forward nor the backward waits for the
+    host, and a captured graph follows the parameter's updates); with the
     stabilisation switches also y_weight[D], out_weight[N·D] and
     pre_weight[N·D] (fp32, initialised to one).  x is [T, N, D] or
     [B, S, N, D], fp32 or bf16, on the GPU.
@@ -161,7 +161,7 @@ class MHCBlock(torch.nn.Module):
         self.N, self.D, self.iters, self.eps, self.recompute = N, D, iters, eps, recompute
         self.phi = torch.nn.Parameter(torch.randn(N * D, C, device=device) / (N * D) ** 0.5)
         self.bias = torch.nn.Parameter(torch.zeros(C, device=device))
-        self.alpha = torch.nn.Parameter(torch.tensor(alpha, dtype=torch.float32),
+        self.alpha = torch.nn.Parameter(torch.tensor(alpha, dtype=torch.float32, device=device),
                                         requires_grad=train_alpha)
         ones = lambda n: torch.nn.Parameter(torch.ones(n, device=device))  # noqa: E731
         self.y_weight = ones(D) if sandwich_norm else None
@@ -207,19 +207,18 @@ class _PostPre(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, x, y, H_post_in, H_res_in, phi, bias, alpha, iters, eps, handoff_in, handoff_out):
-        alphas = tuple(float(a) for a in alpha.tolist())
         x_next, h, Hp, Hq, Hr = mhc.mhc_post_pre(x, y, H_post_in, H_res_in, phi, bias, iters=iters,
-                                                 eps=eps, alphas=alphas)
-        ctx.save_for_backward(x, y, H_post_in, H_res_in, x_next, phi, bias)
-        ctx.cfg = (iters, eps, alphas, alpha.requires_grad)
+                                                 eps=eps, alphas=alpha)
+        ctx.save_for_backward(x, y, H_post_in, H_res_in, x_next, phi, bias, alpha)
+        ctx.cfg = (iters, eps, alpha.requires_grad)
         ctx.handoff_in, ctx.handoff_out = handoff_in, handoff_out
         ctx.mark_non_differentiable(Hp)
         return x_next, h, Hp, Hq, Hr
 
     @staticmethod
     def backward(ctx, dxn, dh, _dHp, dHq, dHr):
-        x, y, H_post_in, H_res_in, x_next, phi, bias = ctx.saved_tensors
-        iters, eps, alphas, want_dalpha = ctx.cfg
+        x, y, H_post_in, H_res_in, x_next, phi, bias, alphas = ctx.saved_tensors
+        iters, eps, want_dalpha = ctx.cfg
         T, N, D = x.shape
         if dh is None:
             dh = torch.zeros((T, D), dtype=x.dtype, device=x.device)
@@ -249,8 +248,7 @@ class _PostPre(torch.autograd.Function):
         else:
             dx, dy, dHq_in, dHr_in = mhc.mhc_post_bwd(dx_next, x, y, H_post_in, H_res_in)
             ctx.handoff_out.dx = dx
-        dalpha = dalpha.cpu() if want_dalpha else None
-        return None, dy, dHq_in, dHr_in, dphi, dbias, dalpha, None, None, None, None
+        return None, dy, dHq_in, dHr_in, dphi, dbias, (dalpha if want_dalpha else None), None, None, None, None
 
 
 class MHCStack(torch.nn.Module):

@@ -101,10 +101,10 @@ hipError_t launch_post_bwd(const mhc_desc& d, const void* dxn, const void* x, co
       constexpr int N = decltype(n_)::value;
       constexpr int IO = decltype(io_)::value;
       if (dx != nullptr)
-        hipLaunchKernelGGL((hc_post_bwd_generic<N, IO, true>), dim3((unsigned)d.T), dim3(kBwdThreads), 0,
+        MHC_LAUNCH((hc_post_bwd_generic<N, IO, true>), dim3((unsigned)d.T), dim3(kBwdThreads), 0,
                            s, dxn, x, y, H_post, H_res, dx, dy, dH_post, dH_res, d.D);
       else
-        hipLaunchKernelGGL((hc_post_bwd_generic<N, IO, false>), dim3((unsigned)d.T), dim3(kBwdThreads),
+        MHC_LAUNCH((hc_post_bwd_generic<N, IO, false>), dim3((unsigned)d.T), dim3(kBwdThreads),
                            0, s, dxn, x, y, H_post, H_res, dx, dy, dH_post, dH_res, d.D);
     });
   });
@@ -151,7 +151,7 @@ static hipError_t launch_res_mix_t(const mhc_desc& d, const void* dxn, const flo
     dispatch_io(d.io, [&](auto io_) {
       constexpr int N = decltype(n_)::value;
       constexpr int IO = decltype(io_)::value;
-      hipLaunchKernelGGL((res_mix_t_kernel<N, IO>), dim3((unsigned)d.T), dim3(kBwdThreads), 0, s, dxn,
+      MHC_LAUNCH((res_mix_t_kernel<N, IO>), dim3((unsigned)d.T), dim3(kBwdThreads), 0, s, dxn,
                          H_res, dx, d.D);
     });
   });
@@ -207,7 +207,12 @@ __global__ __launch_bounds__(kBwdThreads) void hc_pre_bwd_token(
     const float* __restrict__ bias, const float* __restrict__ dH_post_in,
     const float* __restrict__ dH_res_in, void* __restrict__ dx, float* __restrict__ gq_out,
     float* __restrict__ dlog_out, float* __restrict__ dal_out, int D, int iters, float eps,
-    float a_pre, float a_post, float a_res) {
+    float a_pre, float a_post, float a_res, const float* __restrict__ alpha_dev) {
+  if (alpha_dev != nullptr) {  // the gate scalars are held on the device (trained α)
+    a_pre = alpha_dev[0];
+    a_post = alpha_dev[1];
+    a_res = alpha_dev[2];
+  }
   constexpr int C = N * N + 2 * N;
   constexpr int A = C + 1 + N;  // raw p[C], ss, dH_pre[N]
   __shared__ float red[(kBwdThreads / kWave) * A];
@@ -462,19 +467,19 @@ hipError_t launch_pre_bwd(const mhc_desc& d, const void* dh, const void* x, cons
       constexpr int C = N * N + 2 * N;
       constexpr int KPT = N <= 2 ? 8 : (N == 4 ? 4 : 1);
       const size_t rec_bytes = (size_t)2 * d.sinkhorn_iters * (N * N + N) * sizeof(float);
-      hipLaunchKernelGGL((hc_pre_bwd_token<N, IO>), dim3((unsigned)d.T), dim3(kBwdThreads),
+      MHC_LAUNCH((hc_pre_bwd_token<N, IO>), dim3((unsigned)d.T), dim3(kBwdThreads),
                          rec_bytes, s, dh, x, phi, bias, dH_post, dH_res, dx, gq, dlog, dal, d.D,
-                         d.sinkhorn_iters, d.eps, d.alpha_pre, d.alpha_post, d.alpha_res);
+                         d.sinkhorn_iters, d.eps, d.alpha_pre, d.alpha_post, d.alpha_res, d.alpha);
       if ((err = hipGetLastError()) != hipSuccess) return;
       const unsigned gx = (unsigned)((L.K + kBwdThreads * KPT - 1) / (kBwdThreads * KPT));
-      hipLaunchKernelGGL((dphi_partial<N, IO, KPT>), dim3(gx, (unsigned)L.S), dim3(kBwdThreads), 0,
+      MHC_LAUNCH((dphi_partial<N, IO, KPT>), dim3(gx, (unsigned)L.S), dim3(kBwdThreads), 0,
                          s, x, gq, part, (int64_t)d.T, L.K, tok_per_split);
       if ((err = hipGetLastError()) != hipSuccess) return;
       const int64_t KC = (int64_t)L.K * C;
-      hipLaunchKernelGGL(dphi_reduce, dim3((unsigned)((KC + kBwdThreads - 1) / kBwdThreads)),
+      MHC_LAUNCH(dphi_reduce, dim3((unsigned)((KC + kBwdThreads - 1) / kBwdThreads)),
                          dim3(kBwdThreads), 0, s, part, dphi, KC, L.S);
       if ((err = hipGetLastError()) != hipSuccess) return;
-      hipLaunchKernelGGL((bias_alpha_reduce<N>), dim3(1), dim3(kBwdThreads), 0, s, dlog, dal,
+      MHC_LAUNCH((bias_alpha_reduce<N>), dim3(1), dim3(kBwdThreads), 0, s, dlog, dal,
                          dbias, dalpha, (int64_t)d.T);
       err = hipGetLastError();
     });

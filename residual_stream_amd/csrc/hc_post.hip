@@ -50,7 +50,7 @@ hipError_t launch_post(const mhc_desc& d, const void* x, const void* y, const fl
     dispatch_io(d.io, [&](auto io_) {
       constexpr int N = decltype(n_)::value;
       constexpr int IO = decltype(io_)::value;
-      hipLaunchKernelGGL((hc_post_generic<N, IO>), dim3((unsigned)d.T), dim3(kPostThreads), 0, s,
+      MHC_LAUNCH((hc_post_generic<N, IO>), dim3((unsigned)d.T), dim3(kPostThreads), 0, s,
                          x, y, H_post, H_res, x_next, d.D);
     });
   });

@@ -621,7 +621,7 @@ hipError_t launch_post_stable(const mhc_desc& d, const void* x, const void* y, c
   stab::Shape sh;
   if (!stab::shape_for(d.N, d.D, sh)) return hipErrorInvalidValue;
   const bool ok = stab::dispatch(d.N, d.io, sh.cpt, sw, pn, [&](auto n_, auto io_, auto c_, auto sw_, auto pn_) {
-    hipLaunchKernelGGL((stab::post_stable_fwd<decltype(n_)::value, decltype(io_)::value, decltype(c_)::value,
+    MHC_LAUNCH((stab::post_stable_fwd<decltype(n_)::value, decltype(io_)::value, decltype(c_)::value,
                                               decltype(sw_)::value, decltype(pn_)::value>),
                        dim3((unsigned)d.T), dim3(sh.nthr), 0, s, x, y, wy, H_post, H_res, wx, x_next, d.D,
                        d.eps);
@@ -642,7 +642,7 @@ hipError_t launch_post_stable_bwd(const mhc_desc& d, const void* dxn, const void
   if (G < 1) return hipErrorInvalidValue;
   float* part = static_cast<float*>(ws);
   const bool ok = stab::dispatch(d.N, d.io, sh.cpt, sw, pn, [&](auto n_, auto io_, auto c_, auto sw_, auto pn_) {
-    hipLaunchKernelGGL((stab::post_stable_bwd<decltype(n_)::value, decltype(io_)::value, decltype(c_)::value,
+    MHC_LAUNCH((stab::post_stable_bwd<decltype(n_)::value, decltype(io_)::value, decltype(c_)::value,
                                               decltype(sw_)::value, decltype(pn_)::value>),
                        dim3((unsigned)G), dim3(sh.nthr), stab::accx_lds_bytes(d.N, sh.cpt, sh.nthr, pn), s,
                        dxn, x, y, wy, H_post, H_res, wx, dx, dy,
@@ -651,7 +651,7 @@ hipError_t launch_post_stable_bwd(const mhc_desc& d, const void* dxn, const void
   if (!ok) return hipErrorInvalidValue;
   const int Dy = sw ? d.D : 0;
   const int W = Dy + (pn ? d.N * d.D : 0);
-  hipLaunchKernelGGL(stab::stable_wsum, dim3((unsigned)((W + kWave - 1) / kWave)), dim3(stab::kSumWaves * kWave),
+  MHC_LAUNCH(stab::stable_wsum, dim3((unsigned)((W + kWave - 1) / kWave)), dim3(stab::kSumWaves * kWave),
                      0, s, part, G, W, Dy, dwy, dwx);
   return hipGetLastError();
 }

@@ -20,7 +20,12 @@ __global__ __launch_bounds__(kPreThreads) void hc_pre_generic(
     const void* __restrict__ x, const float* __restrict__ phi, const float* __restrict__ bias,
     void* __restrict__ h, float* __restrict__ H_pre, float* __restrict__ H_post,
     float* __restrict__ H_res, int D, int iters, float eps, float a_pre, float a_post,
-    float a_res) {
+    float a_res, const float* __restrict__ alpha_dev) {
+  if (alpha_dev != nullptr) {  // the gate scalars are held on the device (trained α)
+    a_pre = alpha_dev[0];
+    a_post = alpha_dev[1];
+    a_res = alpha_dev[2];
+  }
   constexpr int C = N * N + 2 * N;
   __shared__ float red[(kPreThreads / kWave) * (C + 1)];
   __shared__ float hpre_s[N];
@@ -89,9 +94,9 @@ hipError_t launch_pre_generic(const mhc_desc& d, const void* x, const float* phi
     dispatch_io(d.io, [&](auto io_) {
       constexpr int N = decltype(n_)::value;
       constexpr int IO = decltype(io_)::value;
-      hipLaunchKernelGGL((hc_pre_generic<N, IO>), dim3((unsigned)d.T), dim3(kPreThreads), 0, s,
+      MHC_LAUNCH((hc_pre_generic<N, IO>), dim3((unsigned)d.T), dim3(kPreThreads), 0, s,
                          x, phi, bias, h, H_pre, H_post, H_res, d.D, d.sinkhorn_iters, d.eps,
-                         d.alpha_pre, d.alpha_post, d.alpha_res);
+                         d.alpha_pre, d.alpha_post, d.alpha_res, d.alpha);
     });
   });
   if (!ok) return hipErrorInvalidValue;

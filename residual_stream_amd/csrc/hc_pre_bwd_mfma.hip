@@ -290,7 +290,12 @@ __global__ __launch_bounds__(kCoefThreads) void bwd_coef_kernel(
     const float* __restrict__ part, int nslices, const float* __restrict__ bias,
     const float* __restrict__ dH_post, const float* __restrict__ dH_res, float* __restrict__ coef,
     float* __restrict__ dlog, float* __restrict__ dal, int64_t T, int D, int iters, float eps,
-    float a_pre, float a_post, float a_res) {
+    float a_pre, float a_post, float a_res, const float* __restrict__ alpha_dev) {
+  if (alpha_dev != nullptr) {  // the gate scalars are held on the device (trained α)
+    a_pre = alpha_dev[0];
+    a_post = alpha_dev[1];
+    a_res = alpha_dev[2];
+  }
   extern __shared__ float hist[];  // per lane and round: u_i, then v_i (v_j read from lane j)
   const int lane = threadIdx.x;
   const int i = lane & 3;                 // H_res row owned by this lane
@@ -1193,38 +1198,38 @@ hipError_t launch_pre_bwd_mfma(const mhc_desc& d, const void* dh, const void* x,
   const int K = kN * d.D;
   const dim3 pgrid((unsigned)L.S, (unsigned)L.PS);
   if (d.io == kF32)
-    hipLaunchKernelGGL(bwd_proj_f32_kernel, pgrid, dim3(kFThreads), 0, s, static_cast<const float*>(x),
+    MHC_LAUNCH(bwd_proj_f32_kernel, pgrid, dim3(kFThreads), 0, s, static_cast<const float*>(x),
                        static_cast<const float*>(dh), phi, part, T, d.D, L.R);
   else if (L.W == 10)
-    hipLaunchKernelGGL(bwd_proj_kernel<10>, pgrid, dim3(640), 0, s, static_cast<const uint16_t*>(x),
+    MHC_LAUNCH(bwd_proj_kernel<10>, pgrid, dim3(640), 0, s, static_cast<const uint16_t*>(x),
                        static_cast<const uint16_t*>(dh), phi, part, T, d.D, L.R);
   else
-    hipLaunchKernelGGL(bwd_proj_kernel<8>, pgrid, dim3(512), 0, s, static_cast<const uint16_t*>(x),
+    MHC_LAUNCH(bwd_proj_kernel<8>, pgrid, dim3(512), 0, s, static_cast<const uint16_t*>(x),
                        static_cast<const uint16_t*>(dh), phi, part, T, d.D, L.R);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t hist_bytes = (size_t)d.sinkhorn_iters * 2 * 64 * sizeof(float);
-  hipLaunchKernelGGL(bwd_coef_kernel, dim3((unsigned)((T + 15) / 16)), dim3(kCoefThreads), hist_bytes,
+  MHC_LAUNCH(bwd_coef_kernel, dim3((unsigned)((T + 15) / 16)), dim3(kCoefThreads), hist_bytes,
                      s, part, L.S, bias, dH_post, dH_res, coef, dlog, dal, T, d.D, d.sinkhorn_iters,
-                     d.eps, d.alpha_pre, d.alpha_post, d.alpha_res);
+                     d.eps, d.alpha_pre, d.alpha_post, d.alpha_res, d.alpha);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t tps = ((T + L.TS - 1) / L.TS + kDxTile - 1) / kDxTile * kDxTile;  // tokens per split
   if (d.io == kF32)
-    hipLaunchKernelGGL(bwd_dx_f32_kernel, dim3((unsigned)(d.D / kFD), (unsigned)L.TS), dim3(kFThreads), 0, s,
+    MHC_LAUNCH(bwd_dx_f32_kernel, dim3((unsigned)(d.D / kFD), (unsigned)L.TS), dim3(kFThreads), 0, s,
                        static_cast<const float*>(x), static_cast<const float*>(dh), phi, coef,
                        static_cast<float*>(dx), dphi_part, T, d.D, tps);
   else if (dxn != nullptr)
-    hipLaunchKernelGGL(bwd_dx_kernel<true>, dim3((unsigned)(K / kDxK), (unsigned)L.TS), dim3(kDxThreads), 0,
+    MHC_LAUNCH(bwd_dx_kernel<true>, dim3((unsigned)(K / kDxK), (unsigned)L.TS), dim3(kDxThreads), 0,
                        s, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dh), phi, coef,
                        static_cast<uint16_t*>(dx), dphi_part, T, d.D, tps, static_cast<const uint16_t*>(dxn),
                        H_res);
   else
-    hipLaunchKernelGGL(bwd_dx_kernel<false>, dim3((unsigned)(K / kDxK), (unsigned)L.TS), dim3(kDxThreads), 0,
+    MHC_LAUNCH(bwd_dx_kernel<false>, dim3((unsigned)(K / kDxK), (unsigned)L.TS), dim3(kDxThreads), 0,
                        s, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dh), phi, coef,
                        static_cast<uint16_t*>(dx), dphi_part, T, d.D, tps, nullptr, nullptr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t KC = (int64_t)K * kC;
-  hipLaunchKernelGGL(dphi_bias_sum_kernel, dim3((unsigned)((KC + 255) / 256 + 1)), dim3(256), 0, s,
+  MHC_LAUNCH(dphi_bias_sum_kernel, dim3((unsigned)((KC + 255) / 256 + 1)), dim3(256), 0, s,
                      dphi_part, dphi, KC, L.TS, dlog, dal, dbias, dalpha, (int64_t)((T + 15) / 16));
   return hipGetLastError();
 }

@@ -86,7 +86,12 @@ __global__ __launch_bounds__(kThreads) void pre_decode_finish(
     const void* __restrict__ x, const float* __restrict__ part, int G, const float* __restrict__ bias,
     void* __restrict__ h, float* __restrict__ H_pre, float* __restrict__ H_post,
     float* __restrict__ H_res, int T, int D, int iters, float eps, float a_pre, float a_post,
-    float a_res) {
+    float a_res, const float* __restrict__ alpha_dev) {
+  if (alpha_dev != nullptr) {  // the gate scalars are held on the device (trained α)
+    a_pre = alpha_dev[0];
+    a_post = alpha_dev[1];
+    a_res = alpha_dev[2];
+  }
   constexpr int C = N * N + 2 * N;
   constexpr int kParts = kThreads / (C + 1);  // partial sums per column
   constexpr int kChunk = 16;                   // loads of a thread in flight together
@@ -198,11 +203,11 @@ hipError_t launch_pre_decode(const mhc_desc& d, const void* x, const float* phi,
     dispatch_io(d.io, [&](auto io_) {
       constexpr int N = decltype(n_)::value;
       constexpr int IO = decltype(io_)::value;
-      hipLaunchKernelGGL((decode::pre_decode_partial<N, IO>), dim3((unsigned)G), dim3(decode::kThreads), 0,
+      MHC_LAUNCH((decode::pre_decode_partial<N, IO>), dim3((unsigned)G), dim3(decode::kThreads), 0,
                          s, x, phi, part, (int)d.T, K);
-      hipLaunchKernelGGL((decode::pre_decode_finish<N, IO>), dim3((unsigned)d.T), dim3(decode::kThreads), 0,
+      MHC_LAUNCH((decode::pre_decode_finish<N, IO>), dim3((unsigned)d.T), dim3(decode::kThreads), 0,
                          s, x, part, G, bias, h, H_pre, H_post, H_res, (int)d.T, d.D, d.sinkhorn_iters,
-                         d.eps, d.alpha_pre, d.alpha_post, d.alpha_res);
+                         d.eps, d.alpha_pre, d.alpha_post, d.alpha_res, d.alpha);
     });
   });
   if (!ok) return hipErrorInvalidValue;

@@ -159,7 +159,12 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void hc_pre_mfma_kernel(
     const void* __restrict__ x, const uint4* __restrict__ phip, const float* __restrict__ bias,
     void* __restrict__ h, float* __restrict__ H_pre, float* __restrict__ H_post,
     float* __restrict__ H_res, int64_t T, int iters, float eps, float a_pre, float a_post,
-    float a_res) {
+    float a_res, const float* __restrict__ alpha_dev) {
+  if (alpha_dev != nullptr) {  // the gate scalars are held on the device (trained α)
+    a_pre = alpha_dev[0];
+    a_post = alpha_dev[1];
+    a_res = alpha_dev[2];
+  }
   using P = PreTile<TM>;
   constexpr int R = P::R, SPB = P::SPB, CG = P::CG;
   constexpr int PS = IO == kF32 ? 2 : 1;
@@ -489,16 +494,16 @@ static hipError_t launch_mfma(const mhc_desc& d, const PreConfig& pc, const void
   constexpr int PS = IO == kF32 ? 2 : 1;
   uint4* phip = static_cast<uint4*>(ws);
   const int64_t npack = (int64_t)pc.nsteps * pc.cg * PS * 64;
-  hipLaunchKernelGGL((phi_pack_kernel<TM, PS>), dim3((unsigned)((npack + 255) / 256)), dim3(256),
+  MHC_LAUNCH((phi_pack_kernel<TM, PS>), dim3((unsigned)((npack + 255) / 256)), dim3(256),
                      0, s, phi, phip, d.D, pc.nsteps);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t ntiles = (d.T + TM - 1) / TM;
   const int cus = device_cu_count();
   const int64_t grid = ntiles < cus ? ntiles : cus;
-  hipLaunchKernelGGL((hc_pre_mfma_kernel<IO, TM, NB>), dim3((unsigned)grid), dim3(kMfmaThreads), 0,
+  MHC_LAUNCH((hc_pre_mfma_kernel<IO, TM, NB>), dim3((unsigned)grid), dim3(kMfmaThreads), 0,
                      s, x, phip, bias, h, H_pre, H_post, H_res, (int64_t)d.T,
-                     d.sinkhorn_iters, d.eps, d.alpha_pre, d.alpha_post, d.alpha_res);
+                     d.sinkhorn_iters, d.eps, d.alpha_pre, d.alpha_post, d.alpha_res, d.alpha);
   return hipGetLastError();
 }
 

@@ -7,37 +7,43 @@
 // h = Σ_n H_pre[n]·x[n], which needs the whole-token reduction first.
 //
 // Layout on the chip:
-//  * A tile is M = 32 (or 64) consecutive tokens.  A group of S = 4
+//  * A tile is M = 16, 32 or 64 consecutive tokens.  A group of S = 8 or 4
 //    workgroups (one per CU) takes a tile; workgroup `slice` owns the d range
-//    [slice·D/4, (slice+1)·D/4) of all four streams, so the collapse of its
-//    d range needs no other workgroup's x.  Its share of the tile (M·D
-//    elements, 320 KB at M = 32, D = 5120) stays in VGPRs from the
-//    projection to the collapse: x crosses HBM once.
-//  * Eight waves; a wave owns 160 d of the slice (all four streams: 20 steps
-//    of 32 k) for 16·TBW tokens.  Its registers hold x as the A fragments of
-//    v_mfma_f32_16x16x32_bf16 (lane: token row l mod 16, 8 consecutive d),
-//    so the four streams of a (token, d) sit in one lane and the collapse is
-//    lane-local.
+//    [slice·D/S, (slice+1)·D/S) of all four streams, so the collapse of its
+//    d range needs no other workgroup's x.  Its share of the tile stays in
+//    VGPRs (and AGPRs) from the projection to the collapse: x crosses HBM
+//    once.
+//  * Four or eight waves; a wave owns 160 d of the slice (all four streams:
+//    20 steps of 32 k) for 16·TBW tokens.  Its registers hold x as the A
+//    fragments of v_mfma_f32_16x16x32_bf16 (lane: token row l mod 16, 8
+//    consecutive d), so the four streams of a (token, d) sit in one lane and
+//    the collapse is lane-local.
 //  * φ keeps fp32 accuracy as two bf16 parts, φ = hi + lo (x is exact in
 //    bf16, so x·hi + x·lo carries about 16 mantissa bits of φ into an fp32
 //    accumulation).  A packing kernel writes both parts once per call in the
 //    B-fragment order of the matrix cores: per 32-k step three 16-column
-//    groups [hi 0..15 | hi 16..23, lo 0..7 | lo 8..23], 3 KB, which the wave
-//    streams from L2 alongside x (φ is 2 MB, shared by every group).
+//    groups [hi 0..15 | hi 16..23, lo 0..7 | lo 8..23], 3 KB, which each wave
+//    streams from L2 into a ring of LDS slots with direct-to-LDS loads, five
+//    steps ahead, beside its x loads.
 //  * After the last step each workgroup sums its waves' partials in LDS (fixed
 //    order), publishes 25 numbers per token (24 raw projections and the sum
 //    of squares) as tagged 64-bit records, and gathers the other slices':
 //    pre[4] and the sum of squares of every token of the tile, and post[4],
-//    res[16] of the M/4 tokens it finishes.  Every workgroup derives rstd and
+//    res[16] of the M/S tokens it finishes.  Every workgroup derives rstd and
 //    H_pre of all M tokens (the same arithmetic in the same order, so the
-//    same bits); the finishing one also runs the gates and Sinkhorn (one
-//    token per four lanes, DPP column sums) and writes H_pre, H_post, H_res.
+//    same bits); the finishing one also runs the gates and Sinkhorn (sixteen
+//    lanes per token, one H_res entry each, DPP row and column sums) and
+//    writes H_pre, H_post, H_res.
 //  * Records are 64-bit words (value | 32-bit call tag) written and read with
 //    relaxed device-scope accesses: a reader that sees the tag sees the
-//    value, and stale records of an earlier call never match.  Workgroups
-//    take their roles from tickets (consecutive tickets form a group), so a
-//    group only waits on members that are already running; each wait is
-//    bounded and one that runs out writes NaN for the tile's tokens.
+//    value.  The tag is a per-process seed plus a per-device call number that
+//    the packing kernel of the same call takes from a device-wide counter and
+//    stores in the workspace header, so no two calls of the process on a
+//    device share a tag (until 2^31 calls) whatever memory their workspaces
+//    used before, and a replayed HIP graph gets a new tag on every replay.
+//    Workgroups take their roles from tickets (consecutive tickets form a
+//    group), so a group only waits on members that are already running; each
+//    wait is bounded and one that runs out writes NaN for the tile's tokens.
 #include "mhc_coef.h"
 #include "mhc_internal.h"
 
@@ -58,8 +64,10 @@ constexpr int kWaveD = kDB * 32;     // d per wave (160)
 constexpr int kCG = 3;               // B column groups per step
 constexpr int kCols = 16 * kCG;      // hi[0..24) then lo[0..24)
 constexpr int kAhead = 5;            // steps whose loads are in flight
-constexpr int kHeader = 256;         // workspace bytes holding the ticket counter
+constexpr int kHeader = 256;         // workspace bytes: ticket counter, call number
 constexpr uint32_t kSpinLimit = 1u << 20;
+// calls of the split-K hc_pre on this device so far (one copy per device)
+__device__ uint64_t g_calls = 0;
 static_assert(kSteps % kN == 0, "each step is 32 d of one stream");
 
 __device__ __forceinline__ f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
@@ -156,19 +164,41 @@ __device__ __forceinline__ void each(F&& f, std::integer_sequence<int, J...>) {
 // jd = j mod 5; wave wd of slice sl, dw = sl·WD + wd; WD waves along d) of
 // column cg = 0: hi(c); cg = 1: c < 8 ? hi(16 + c) : lo(c − 8); cg = 2:
 // lo(8 + c); hi = bf16(φ), lo = bf16(φ − hi), both rounded to nearest even.
-// One workgroup per (dw, j): the 32 rows are 3 KB of consecutive φ, read as
-// one coalesced run into LDS; the three fragments (3 KB) go out the same way.
+// A workgroup packs kPackItems consecutive (dw, j) fragments: each is 32
+// rows, 3 KB of consecutive φ, read as one coalesced run into LDS (every
+// item's loads issued before the first is used); the three fragments (3 KB)
+// go out the same way.
 constexpr int kPackThreads = kCG * 64;
+constexpr int kPackItems = 4;
 __global__ __launch_bounds__(kPackThreads) void phi_pack_tile_kernel(const float* __restrict__ phi,
-                                                                     uint4* __restrict__ out, int D, int WD) {
-  __shared__ float rows_s[32 * kC];
-  const int j = blockIdx.x % kSteps, dw = blockIdx.x / kSteps;
-  const int n = j / kDB, jd = j % kDB;
-  // wave wd of slice sl takes the slice's 32-d blocks wd, wd + WD, wd + 2·WD, …
-  const int sl = dw / WD, wd = dw % WD;
-  const int64_t k0 = (int64_t)n * D + (int64_t)sl * (WD * kWaveD) + 32 * (jd * WD + wd);
-  static_assert(32 * kC == 4 * kPackThreads, "one float4 per thread");
-  reinterpret_cast<float4*>(rows_s)[threadIdx.x] = reinterpret_cast<const float4*>(phi + k0 * kC)[threadIdx.x];
+                                                                     uint4* __restrict__ out, int D, int WD,
+                                                                     uint64_t* call_no) {
+  // every call takes a number of its own from the device-wide counter, before
+  // the main kernel starts, and leaves it in its workspace header: the main
+  // kernel tags its records with it (also on every replay of a HIP graph)
+  if (blockIdx.x == 0 && threadIdx.x == 0)
+    __hip_atomic_store(call_no, __hip_atomic_fetch_add(&g_calls, (uint64_t)1, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT) + 1,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __shared__ float rows_s[kPackItems][32 * kC];
+  static_assert(32 * kC == 4 * kPackThreads, "one float4 per thread and item");
+  const int nitems = D / kWaveD * kSteps;
+  float4 v[kPackItems];
+#pragma unroll
+  for (int q = 0; q < kPackItems; ++q) {
+    const int item = blockIdx.x * kPackItems + q;
+    v[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (item < nitems) {
+      const int j = item % kSteps, dw = item / kSteps;
+      const int n = j / kDB, jd = j % kDB;
+      // wave wd of slice sl takes the slice's 32-d blocks wd, wd + WD, wd + 2·WD, …
+      const int sl = dw / WD, wd = dw % WD;
+      const int64_t k0 = (int64_t)n * D + (int64_t)sl * (WD * kWaveD) + 32 * (jd * WD + wd);
+      v[q] = reinterpret_cast<const float4*>(phi + k0 * kC)[threadIdx.x];
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < kPackItems; ++q) reinterpret_cast<float4*>(rows_s[q])[threadIdx.x] = v[q];
   __syncthreads();
   const int cg = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c = lane & 15, gq = lane >> 4;
@@ -184,15 +214,20 @@ __global__ __launch_bounds__(kPackThreads) void phi_pack_tile_kernel(const float
     col = 8 + c;
     lo = true;
   }
-  uint32_t w[4];
 #pragma unroll
-  for (int v = 0; v < 8; v += 2) {
-    const float f0 = rows_s[(8 * gq + v) * kC + col], f1 = rows_s[(8 * gq + v + 1) * kC + col];
-    uint32_t hw = pack_bf16x2(f0, f1);
-    if (lo) hw = pack_bf16x2(f0 - bf16_lo(hw), f1 - bf16_hi(hw));
-    w[v / 2] = hw;
+  for (int q = 0; q < kPackItems; ++q) {
+    const int item = blockIdx.x * kPackItems + q;
+    if (item >= nitems) break;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const float f0 = rows_s[q][(8 * gq + e) * kC + col], f1 = rows_s[q][(8 * gq + e + 1) * kC + col];
+      uint32_t hw = pack_bf16x2(f0, f1);
+      if (lo) hw = pack_bf16x2(f0 - bf16_lo(hw), f1 - bf16_hi(hw));
+      w[e / 2] = hw;
+    }
+    out[(int64_t)item * kPackThreads + threadIdx.x] = make_uint4(w[0], w[1], w[2], w[3]);
   }
-  out[(int64_t)blockIdx.x * kPackThreads + threadIdx.x] = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // ------------------------------------------------------------ main kernel ---
@@ -205,7 +240,12 @@ __global__ __launch_bounds__(W * 64, 1) void hc_pre_tile_kernel(
     const uint16_t* __restrict__ x, const uint4* __restrict__ phip, const float* __restrict__ bias,
     uint16_t* __restrict__ h, float* __restrict__ H_pre, float* __restrict__ H_post,
     float* __restrict__ H_res, uint64_t* ctr, uint64_t* rec, int64_t T, int Q, uint32_t tag,
-    int iters, float eps, float a_pre, float a_post, float a_res) {
+    int iters, float eps, float a_pre, float a_post, float a_res, const float* __restrict__ alpha_dev) {
+  if (alpha_dev != nullptr) {  // the gate scalars are held on the device (trained α)
+    a_pre = alpha_dev[0];
+    a_post = alpha_dev[1];
+    a_res = alpha_dev[2];
+  }
   constexpr int kS = S, kWaves = W, kThreads = W * 64;
   constexpr int WT = kWaves / WD;
   constexpr int M = 16 * TBW * WT;      // tokens per tile
@@ -226,12 +266,17 @@ __global__ __launch_bounds__(W * 64, 1) void hc_pre_tile_kernel(
   __shared__ float fin_s[F][kN * kN];                 // res logits of the tokens this workgroup finishes
   __shared__ float bias_s[kC];
   __shared__ int ticket_s;
+  __shared__ uint32_t tag_s;
 
-  if (threadIdx.x == 0)
+  if (threadIdx.x == 0) {
     ticket_s = (int)(__hip_atomic_fetch_add(ctr, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) %
                      gridDim.x);
+    // process seed + this call's number
+    tag_s = (tag + (uint32_t)__hip_atomic_load(ctr + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) | 0x80000000u;
+  }
   if (threadIdx.x < kC) bias_s[threadIdx.x] = bias[threadIdx.x];
   __syncthreads();
+  tag = tag_s;
   const int ticket = ticket_s;
   const int grp = ticket / kS, slice = ticket % kS;
   if (grp >= Q) return;
@@ -582,22 +627,23 @@ hipError_t launch_pre_tile(const mhc_desc& d, const void* x, const float* phi, c
   uint64_t* ctr = reinterpret_cast<uint64_t*>(w);
   uint4* phip = reinterpret_cast<uint4*>(w + tile::kHeader);
   uint64_t* rec = reinterpret_cast<uint64_t*>(w + tile::kHeader + phi_pack_bytes(d));
-  hipLaunchKernelGGL(tile::phi_pack_tile_kernel, dim3((unsigned)(d.D / tile::kWaveD * tile::kSteps)),
-                     dim3(tile::kPackThreads), 0, s, phi, phip, d.D, c.wd);
+  const int nitems = d.D / tile::kWaveD * tile::kSteps;
+  MHC_LAUNCH(tile::phi_pack_tile_kernel, dim3((unsigned)((nitems + tile::kPackItems - 1) / tile::kPackItems)),
+                     dim3(tile::kPackThreads), 0, s, phi, phip, d.D, c.wd, ctr + 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const uint32_t tag = next_call_tag();
+  const uint32_t tag = process_tag_seed();
   const dim3 grid((unsigned)(Q * c.s)), block((unsigned)(c.w * 64));
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   uint16_t* hp = static_cast<uint16_t*>(h);
 #define MHC_TILE_ARGS                                                                                    \
   grid, block, 0, s, xp, phip, bias, hp, H_pre, H_post, H_res, ctr, rec, (int64_t)d.T, Q, tag, d.sinkhorn_iters, \
-      d.eps, d.alpha_pre, d.alpha_post, d.alpha_res
-  if (c.s == 8) hipLaunchKernelGGL((tile::hc_pre_tile_kernel<8, 4, 4, 4>), MHC_TILE_ARGS);
-  else if (c.w == 4) hipLaunchKernelGGL((tile::hc_pre_tile_kernel<4, 4, 4, 4>), MHC_TILE_ARGS);
-  else if (c.wd == 8 && c.tbw == 2) hipLaunchKernelGGL((tile::hc_pre_tile_kernel<4, 8, 8, 2>), MHC_TILE_ARGS);
-  else if (c.wd == 8) hipLaunchKernelGGL((tile::hc_pre_tile_kernel<4, 8, 8, 1>), MHC_TILE_ARGS);
-  else hipLaunchKernelGGL((tile::hc_pre_tile_kernel<4, 8, 4, 1>), MHC_TILE_ARGS);
+      d.eps, d.alpha_pre, d.alpha_post, d.alpha_res, d.alpha
+  if (c.s == 8) MHC_LAUNCH((tile::hc_pre_tile_kernel<8, 4, 4, 4>), MHC_TILE_ARGS);
+  else if (c.w == 4) MHC_LAUNCH((tile::hc_pre_tile_kernel<4, 4, 4, 4>), MHC_TILE_ARGS);
+  else if (c.wd == 8 && c.tbw == 2) MHC_LAUNCH((tile::hc_pre_tile_kernel<4, 8, 8, 2>), MHC_TILE_ARGS);
+  else if (c.wd == 8) MHC_LAUNCH((tile::hc_pre_tile_kernel<4, 8, 8, 1>), MHC_TILE_ARGS);
+  else MHC_LAUNCH((tile::hc_pre_tile_kernel<4, 8, 4, 1>), MHC_TILE_ARGS);
 #undef MHC_TILE_ARGS
   return hipGetLastError();
 }

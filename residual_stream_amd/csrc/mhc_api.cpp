@@ -28,13 +28,16 @@ int device_cu_count() {
   return n;
 }
 
-// Tags of the exchange records of the split-K kernels: one per call, not
-// repeated for 2^31 calls in a process; the top bit is set so that zeroed
-// memory never matches.
-uint32_t next_call_tag() {
-  static std::atomic<uint32_t> counter{
-      (uint32_t)((uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761u)};
-  return counter.fetch_add(1, std::memory_order_relaxed) | 0x80000000u;
+thread_local KernelTrace g_kernel_trace;
+
+// Seed of the split-K exchange tags: the device adds each call's number to
+// it, and sets the top bit so that zeroed memory never matches.  Drawn from
+// the clock once per load of the library, so that a reloaded library (whose
+// device counters start again at zero) most likely tags differently.
+uint32_t process_tag_seed() {
+  static const uint32_t seed =
+      (uint32_t)((uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761u);
+  return seed;
 }
 
 }  // namespace mhc
@@ -55,8 +58,9 @@ mhc_status check_desc(const mhc_desc* d) {
   if (d->io != MHC_F32 && d->io != MHC_BF16) return MHC_ERR_INVALID_ARG;
   if (d->sinkhorn_iters < 1) return MHC_ERR_INVALID_ARG;
   if (!finite(d->eps) || d->eps < 0.f) return MHC_ERR_INVALID_ARG;
-  if (!finite(d->alpha_pre) || !finite(d->alpha_post) || !finite(d->alpha_res))
+  if (d->alpha == nullptr && (!finite(d->alpha_pre) || !finite(d->alpha_post) || !finite(d->alpha_res)))
     return MHC_ERR_INVALID_ARG;
+  if (d->alpha != nullptr && (reinterpret_cast<uintptr_t>(d->alpha) & 3u) != 0) return MHC_ERR_INVALID_ARG;
   if (d->N != 1 && d->N != 2 && d->N != 4 && d->N != 8) return MHC_ERR_UNSUPPORTED;
   if (d->D < 8 || d->D % 8 != 0 || d->D > (1 << 24)) return MHC_ERR_UNSUPPORTED;
   if (d->sinkhorn_iters > kMaxIters) return MHC_ERR_UNSUPPORTED;
@@ -84,6 +88,18 @@ mhc_status from_hip(hipError_t e) { return e == hipSuccess ? MHC_OK : MHC_ERR_HI
 extern "C" {
 
 int mhc_abi_version(void) { return MHC_ABI_VERSION; }
+
+mhc_status mhc_trace_kernel_events(hipEvent_t* events, const char** names, int capacity, int* count) {
+  if (capacity < 0 || (events != nullptr && capacity == 0)) return MHC_ERR_INVALID_ARG;
+  mhc::KernelTrace& t = mhc::g_kernel_trace;
+  t.events = events;
+  t.names = events != nullptr ? names : nullptr;
+  t.capacity = events != nullptr ? capacity : 0;
+  t.count = events != nullptr ? count : nullptr;
+  t.n = 0;
+  if (t.count != nullptr) *t.count = 0;
+  return MHC_OK;
+}
 
 const char* mhc_status_string(mhc_status s) {
   switch (s) {

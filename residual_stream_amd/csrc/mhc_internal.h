@@ -9,12 +9,49 @@
 
 namespace mhc {
 
+// Kernel-level tracing (mhc_trace_kernel_events): per host thread, an array of
+// caller-owned event pairs recorded around each launch, with the kernels'
+// names.  Off (events == nullptr) unless a caller turns it on.
+struct KernelTrace {
+  hipEvent_t* events = nullptr;
+  const char** names = nullptr;
+  int capacity = 0;
+  int* count = nullptr;
+  int n = 0;
+};
+extern thread_local KernelTrace g_kernel_trace;
+
+inline void trace_before(hipStream_t s) {
+  KernelTrace& t = g_kernel_trace;
+  if (t.events != nullptr && t.n < t.capacity) (void)hipEventRecord(t.events[2 * t.n], s);
+}
+inline void trace_after(hipStream_t s, const char* name) {
+  KernelTrace& t = g_kernel_trace;
+  if (t.events == nullptr || t.n >= t.capacity) return;
+  (void)hipEventRecord(t.events[2 * t.n + 1], s);
+  if (t.names != nullptr) t.names[t.n] = name;
+  ++t.n;
+  if (t.count != nullptr) *t.count = t.n;
+}
+
+// Every kernel of the library is launched through this: hipLaunchKernelGGL
+// with the tracing hooks around it.  Arguments as for hipLaunchKernelGGL
+// (kernel, grid, block, shared bytes, stream, kernel arguments...).
+#define MHC_STREAM_OF_(grid, block, shmem, stream, ...) stream
+#define MHC_LAUNCH(kernel, ...)                                   \
+  do {                                                            \
+    ::mhc::trace_before(MHC_STREAM_OF_(__VA_ARGS__));             \
+    hipLaunchKernelGGL(kernel, __VA_ARGS__);                      \
+    ::mhc::trace_after(MHC_STREAM_OF_(__VA_ARGS__), #kernel);     \
+  } while (0)
+
 // Compute units of the current device (cached per device; a property query,
 // not mutable state).
 int device_cu_count();
 
-// A fresh tag for the exchange records of one split-K call (top bit set).
-uint32_t next_call_tag();
+// Seed of the exchange-record tags of the split-K hc_pre, drawn once per
+// process (each call adds a per-device call number on the device).
+uint32_t process_tag_seed();
 
 // hc_pre with whole token tiles held on chip, the reduction split over groups
 // of four workgroups (bf16, N = 4, D = 5120 or 2560); φ packed into the
@@ -30,8 +67,6 @@ hipError_t launch_pre(const mhc_desc& d, const void* x, const float* phi, const 
                       void* h, float* H_pre, float* H_post, float* H_res, void* ws,
                       hipStream_t s);
 
-// Split-K hc_pre across workgroups (bf16, N = 4, D = 5120 or 2560): groups of
-// workgroups exchange partial sums through the workspace.
 // few-token (decode-sized) hc_pre: k split across the chip, two launches
 constexpr int64_t kDecodeMaxT = 64;
 bool pre_decode_eligible(const mhc_desc& d);
@@ -39,18 +74,8 @@ size_t pre_decode_workspace_bytes(const mhc_desc& d);
 hipError_t launch_pre_decode(const mhc_desc& d, const void* x, const float* phi, const float* bias,
                              void* h, float* H_pre, float* H_post, float* H_res, void* ws,
                              hipStream_t s);
-bool pre_coop_eligible(const mhc_desc& d);
-size_t pre_coop_workspace_bytes(const mhc_desc& d);
-hipError_t launch_pre_coop(const mhc_desc& d, const void* x, const float* phi, const float* bias,
-                           void* h, float* H_pre, float* H_post, float* H_res, void* ws,
-                           hipStream_t s);
-// hc_post of one layer fused with hc_pre of the next (bf16, N = 4, D = 5120 or 2560)
-hipError_t launch_post_pre_coop(const mhc_desc& d, const void* x, const void* y, const float* H_post_in,
-                                const float* H_res_in, void* x_next, const float* phi, const float* bias,
-                                void* h, float* H_pre, float* H_post, float* H_res, void* ws,
-                                hipStream_t s);
 
-// hc_post then hc_pre on its output: fused for the split-K shapes, else the two kernels
+// hc_post then hc_pre on its output (the two kernels, one after the other)
 hipError_t launch_post_pre(const mhc_desc& d, const void* x, const void* y, const float* H_post_in,
                            const float* H_res_in, void* x_next, const float* phi, const float* bias,
                            void* h, float* H_pre, float* H_post, float* H_res, void* ws, hipStream_t s);

@@ -75,7 +75,7 @@ def test_block_matches_oracle(io, T, D):
     assert_close("dx", host(x.grad), dx_post + pre["dx"], tol)
     assert_close("dphi", host(block.phi.grad), pre["dphi"], tol)
     assert_close("dbias", host(block.bias.grad), pre["dbias"], tol)
-    assert_close("dalpha", block.alpha.grad.double().numpy(), pre["dalpha"], tol)
+    assert_close("dalpha", block.alpha.grad.double().cpu().numpy(), pre["dalpha"], tol)
 
 
 def test_recompute_gives_identical_gradients():
@@ -142,7 +142,7 @@ def test_stabilised_block_matches_oracle(io, T, D):
     assert_close("dx", host(x.grad), post["dx"] + pb["dx"], tol)
     assert_close("dphi", host(block.phi.grad), pb["dphi"], tol)
     assert_close("dbias", host(block.bias.grad), pb["dbias"], tol)
-    assert_close("dalpha", block.alpha.grad.double().numpy(), pb["dalpha"], tol)
+    assert_close("dalpha", block.alpha.grad.double().cpu().numpy(), pb["dalpha"], tol)
     assert_close("dy_weight", host(block.y_weight.grad), post["dy_weight"], tol)
     assert_close("dout_weight", host(block.out_weight.grad), post["dout_weight"], tol)
     assert_close("dpre_weight", host(block.pre_weight.grad), pb["dnorm_weight"], tol)
@@ -200,3 +200,62 @@ def test_stack_rejects_stabilised_blocks():
     b = MHCBlock(torch.nn.Identity(), 4, 64, sandwich_norm=True)
     with pytest.raises(ValueError):
         MHCStack([b, MHCBlock(torch.nn.Identity(), 4, 64)])
+
+
+def test_block_forward_backward_captured_in_a_graph():
+    # forward + backward of a block with a trained α captured in one HIP graph
+    # (no host synchronisation anywhere in either direction); every replay on
+    # new inputs equals the eager step, outputs and all four gradients
+    from residual_stream_amd.autograd import MHCBlock
+
+    _say("[autograd] block forward + backward in a graph")
+    T, N, D, io = 130, 4, 5120, "bf16"
+    sets = [make_inputs(T, N, D, io=io, seed=60 + k, alpha=0.3, grads=True) for k in range(3)]
+    c = dev(_scale_vector(sets[0]), io)
+    block = MHCBlock(_Scale(c), N, D, iters=20, eps=1e-6, alpha=(0.3, 0.2, 0.4), train_alpha=True)
+    with torch.no_grad():
+        block.phi.copy_(dev(sets[0].phi))
+        block.bias.copy_(dev(sets[0].bias))
+    x_s = dev(sets[0].x, io).requires_grad_(True)
+    g_s = dev(sets[0].dx_next, io)
+    params = (block.phi, block.bias, block.alpha)
+
+    def step():
+        out = block(x_s)
+        out.backward(g_s)
+        return out
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            for p in params + (x_s,):
+                p.grad = None
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    for p in params + (x_s,):
+        p.grad = None
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out_s = step()
+    for rep in range(5):
+        src = sets[rep % 3]
+        with torch.no_grad():
+            x_s.copy_(dev(src.x, io))
+            g_s.copy_(dev(src.dx_next, io))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [out_s.clone()] + [t.grad.clone() for t in (x_s,) + params]
+        # the eager step on the same inputs, into fresh gradients
+        saved = [t.grad for t in (x_s,) + params]
+        for t in (x_s,) + params:
+            t.grad = None
+        ref = [step().detach().clone()] + [t.grad.clone() for t in (x_s,) + params]
+        torch.cuda.synchronize()
+        for t, s_ in zip((x_s,) + params, saved):
+            t.grad = s_
+        for name, a, b in zip(("x_next", "dx", "dphi", "dbias", "dalpha"), got, ref):
+            a_ = a.view(torch.int16) if a.dtype == torch.bfloat16 else a
+            b_ = b.view(torch.int16) if b.dtype == torch.bfloat16 else b
+            assert torch.equal(a_, b_), f"replay {rep}: {name} differs from the eager step"

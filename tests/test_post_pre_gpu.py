@@ -145,3 +145,56 @@ def test_graph_replay_with_cleared_workspace_matches_eager():
             _bitwise(f"replay {rep} pre {name}", a, b)
         for name, a, b in zip(NAMES, out_pp, ref_pp):
             _bitwise(f"replay {rep} post_pre {name}", a, b)
+
+
+def test_graph_replay_with_uncleared_caller_workspace_matches_eager():
+    # a caller's workspace, never zero-filled, captured with the calls: the
+    # exchange tags still change on every replay (the packing kernel of each
+    # call advances an epoch in the workspace), so replays on new inputs equal
+    # the eager calls bit for bit
+    _say("[graph] caller workspace, not cleared")
+    T, N, D = 300, 4, 5120
+    sets = [make_inputs(T, N, D, io="bf16", seed=s, alpha=1.0) for s in (41, 42, 43)]
+    x = dev(sets[0].x, "bf16")
+    phi, bias = dev(sets[0].phi), dev(sets[0].bias)
+    kw = dict(iters=sets[0].iters, eps=sets[0].eps, alphas=sets[0].alphas)
+    out_pre = (torch.empty((T, D), dtype=torch.bfloat16, device="cuda"), torch.empty((T, N), device="cuda"),
+               torch.empty((T, N), device="cuda"), torch.empty((T, N, N), device="cuda"))
+    ws = torch.full((mhc.workspace_bytes("pre", T, N, D, mhc.MHC_BF16),), 0x5A, dtype=torch.uint8, device="cuda")
+    mhc.mhc_pre(x, phi, bias, out=out_pre, workspace=ws, **kw)  # warm-up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mhc.mhc_pre(x, phi, bias, out=out_pre, workspace=ws, **kw)
+    for rep in range(6):
+        src = sets[rep % 3]
+        x.copy_(dev(src.x, "bf16"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = mhc.mhc_pre(x, phi, bias, **kw)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("h", "H_pre", "H_post", "H_res"), out_pre, ref):
+            _bitwise(f"replay {rep} {name}", a, b)
+
+
+def test_uncleared_workspaces_over_earlier_calls_records_match_fresh_ones():
+    # one buffer, never cleared, serves as the workspace at shifting offsets,
+    # so each call finds records, headers and packed φ of earlier calls (on
+    # other inputs) at every position of its own workspace; each result must
+    # equal that of a call on a zeroed workspace of its own, bit for bit
+    _say("[workspace] uncleared buffer at shifting offsets")
+    T, N, D = 300, 4, 5120
+    sets = [make_inputs(T, N, D, io="bf16", seed=s, alpha=1.0) for s in (51, 52, 53)]
+    kw = dict(iters=sets[0].iters, eps=sets[0].eps, alphas=sets[0].alphas)
+    need = mhc.workspace_bytes("pre", T, N, D, mhc.MHC_BF16)
+    big = torch.full((need + 64 * 256,), 0x5A, dtype=torch.uint8, device="cuda")
+    xs = [dev(s.x, "bf16") for s in sets]
+    phi, bias = dev(sets[0].phi), dev(sets[0].bias)
+    for k, off in enumerate((0, 256, 4096, 0, 512, 256, 8192, 0, 768, 4096, 1024, 0, 16128, 256)):
+        x = xs[k % 3]
+        got = mhc.mhc_pre(x, phi, bias, workspace=big[off:off + need], **kw)
+        ref = mhc.mhc_pre(x, phi, bias, workspace=torch.zeros(need, dtype=torch.uint8, device="cuda"), **kw)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("h", "H_pre", "H_post", "H_res"), got, ref):
+            _bitwise(f"call {k} (offset {off}) {name}", a, b)

@@ -2,17 +2,17 @@
 where their own structure can go wrong.
 
 The split-K forward (bf16, N = 4, D = 5120 or 2560) cuts each token's
-reduction into S = D/320 slices; a group of S workgroups walks the tiles
-grp, grp + Q, grp + 2Q, ... (16 tokens each, Q = compute units / S), keeps
-x in a ring of register buffers until the token's H_pre is known, and runs
-the gates and Sinkhorn of the tokens a workgroup finishes in batches that
-span 16/(16/S) of the group's tiles.  A token's coefficients sent to the wrong
-token, a ring slot taken out of turn, or a batch written to the wrong rows
-only shows where the projection matters: at alpha = 1 (at the workloads'
-alpha = 0.01 the logits are almost the bias, the same for every token).  So
-these cases run at alpha = 1, at full size, with sampled tokens that cover a
-whole tile at both ends of a group and every token of one workgroup's
-Sinkhorn batches, on both sides of a ragged end.
+reduction into S slices of d (S = 8 or 4); a group of S workgroups walks the
+tiles grp, grp + Q, grp + 2Q, ... (M = 16, 32 or 64 tokens each, Q = compute
+units / S), holds the tile's x on chip from the projection to the collapse,
+and workgroup `slice` of the group runs the gates and Sinkhorn of tokens
+slice·M/S .. (slice+1)·M/S − 1 of each tile.  A token's coefficients sent to
+the wrong token, a tile's records mixed with another's, or a finishing share
+written to the wrong rows only shows where the projection matters: at alpha
+= 1 (at the workloads' alpha = 0.01 the logits are almost the bias, the same
+for every token).  So these cases run at alpha = 1, at full size, with
+sampled tokens that cover a whole tile at both ends of a group and every
+token one workgroup finishes, on both sides of a ragged end.
 
 The Sinkhorn round count and order (openPangu 2.0 analysis, §5.3: rows then
 columns, 20 rounds in the model) are pinned with large logits (bias standard
@@ -42,8 +42,8 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
 
 FWD_KEYS = ("h", "H_pre", "H_post", "H_res", "x_next")
 BWD_KEYS = ("dx", "dy", "dH_post", "dH_res", "dphi", "dbias", "dalpha")
-TILE = 16
-SLICE_D = 320
+TILE = 16  # tokens per tile of the tiled backward
+SLICE_D_PER_WAVE = 160  # d per wave of the split-K forward
 
 
 def _say(msg):
@@ -55,24 +55,40 @@ def _cus():
     return torch.cuda.get_device_properties(0).multi_processor_count
 
 
+def tile_config(T, D):
+    """(S, M, Q): the split-K forward's slices per group, tile size and number
+    of groups for T tokens of width D, chosen as the library chooses them
+    (the candidate that leaves each compute unit the least work)."""
+    cus = _cus()
+    best = None
+    for s_, wd, m in ((8, 4, 64), (4, 8, 32), (4, 8, 16), (4, 4, 64), (4, 4, 32)):
+        if s_ * wd * SLICE_D_PER_WAVE != D:
+            continue
+        q = cus // s_
+        ntiles = (T + m - 1) // m
+        work = (ntiles + q - 1) // q * m // s_
+        if best is None or work < best[0]:
+            best = (work, s_, m, q)
+    return best[1:]
+
+
 def split_k_tokens(T, D, grp=3, slice_=5, extra=24, seed=0):
     """Tokens that exercise the split-K kernel's structure: all tokens of the
     first and the last tile of group `grp`, every token workgroup (grp,
-    slice_) finishes (its Sinkhorn batches), the last two tokens and a random
+    slice_) finishes in each of its tiles, the last two tokens and a random
     handful."""
-    S = D // SLICE_D
-    Q = _cus() // S
-    share = TILE // S
-    ntiles = (T + TILE - 1) // TILE
+    S, M, Q = tile_config(T, D)
+    share = M // S
+    ntiles = (T + M - 1) // M
     grp = min(grp, Q - 1, ntiles - 1)
     slice_ = slice_ % S
     nloc = (ntiles - grp + Q - 1) // Q
     toks = set()
     for tile in (grp, grp + (nloc - 1) * Q):
-        toks.update(range(tile * TILE, min(T, tile * TILE + TILE)))
+        toks.update(range(tile * M, min(T, tile * M + M)))
     for p in range(nloc):
         for u in range(share):
-            toks.add((grp + p * Q) * TILE + slice_ * share + u)
+            toks.add((grp + p * Q) * M + slice_ * share + u)
     toks.update((0, T - 2, T - 1))
     rng = np.random.default_rng(seed)
     toks.update(rng.choice(T, extra, replace=False).tolist())

@@ -8,6 +8,7 @@ workgroups that walk several tokens, and the full 4096-token Pro shape."""
 
 from __future__ import annotations
 
+import ctypes
 import sys
 
 import numpy as np
@@ -163,13 +164,23 @@ def test_argument_errors():
     inp, Hq, Hr, wy, wx = _case("bf16", 4, 256, 5, seed=1)
     x, y, Hq_d, Hr_d = dev(inp.x, "bf16"), dev(inp.y, "bf16"), dev(Hq), dev(Hr)
     dxn = dev(inp.dx_next, "bf16")
-    # a weight gradient must be given exactly when its weight is
+    # a weight gradient must be given exactly when its weight is (the
+    # binding refuses the call before the library sees it)
     T, N, D = x.shape
     f32 = dict(dtype=torch.float32, device="cuda")
     out = (torch.empty_like(x), torch.empty_like(y), torch.empty((T, N), **f32),
            torch.empty((T, N, N), **f32), None, None)
-    with pytest.raises(mhc.MhcError):
+    with pytest.raises(ValueError, match="dy_weight"):
         mhc.mhc_post_stable_bwd(dxn, x, y, Hq_d, Hr_d, y_weight=dev(wy), out=out)
+    # ... and the library refuses it too, called through the C ABI directly
+    lib, wy_d = mhc.load(), dev(wy)
+    d = mhc.desc_for(x)
+    ws = torch.empty(mhc.workspace_bytes("post_stable_bwd", T, N, D, mhc.MHC_BF16, y_weight=True) + 256,
+                     dtype=torch.uint8, device="cuda")
+    st = lib.mhc_post_stable_bwd(ctypes.byref(d), dxn.data_ptr(), x.data_ptr(), y.data_ptr(), wy_d.data_ptr(),
+                                 Hq_d.data_ptr(), Hr_d.data_ptr(), None, out[0].data_ptr(), out[1].data_ptr(),
+                                 None, None, out[2].data_ptr(), out[3].data_ptr(), ws.data_ptr(), ws.numel(), None)
+    assert st == mhc.MHC_ERR_INVALID_ARG
     # too small a workspace
     with pytest.raises(mhc.MhcError):
         mhc.mhc_post_stable_bwd(dxn, x, y, Hq_d, Hr_d, y_weight=dev(wy),
