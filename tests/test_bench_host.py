@@ -49,9 +49,35 @@ def test_algorithmic_bytes_of_the_pro_shape():
     assert two - mix == T * K * e - T * N * N * 4
 
 
-def test_every_timed_call_names_its_kernels():
+def test_kernel_names_as_the_library_reports_them():
     b = _bench()
-    ab = b.algo_bytes(64, 4, 256, "bf16")
-    for table in (b.CALL_KERNELS, b.CALL_KERNELS_F32):
-        assert set(table) == set(ab) - {"mhc_post_pre"}
-        assert all(table[k] for k in table)
+    assert b.short_name("(tile::hc_pre_tile_kernel<8, 4, 4, 4>)") == "hc_pre_tile_kernel<8, 4, 4, 4>"
+    assert b.short_name("tile::phi_pack_tile_kernel") == "phi_pack_tile_kernel"
+    assert b.short_name("(hc_post_bwd_generic<N, IO, true>)") == "hc_post_bwd_generic<N, IO, true>"
+    assert b.short_name("bwd_dx_kernel<true>") == "bwd_dx_kernel<true>"
+
+
+def test_kernel_bytes_add_up_to_the_calls():
+    # the kernels of each call together move the call's algorithmic bytes
+    # (φ packing reads φ and writes its copy; the backward's φ read is
+    # counted in the projection and in the dx pass, its dφ in the final sum)
+    b = _bench()
+    T, N, D = 4096, 4, 5120
+    K, C = N * D, N * N + 2 * N
+    phi = K * C * 4
+    for io in ("bf16", "f32"):
+        ab = b.algo_bytes(T, N, D, io)
+        kb = lambda n: b.kernel_bytes(n, T, N, D, io)  # noqa: E731
+        assert kb("hc_pre_tile_kernel<8, 4, 4, 4>") == ab["mhc_pre"]
+        assert kb("hc_pre_mfma_kernel<IO, TM>") == ab["mhc_pre"]
+        assert kb("hc_post_generic<N, IO>") == ab["mhc_post"]
+        assert kb("hc_post_bwd_generic<N, IO, true>") == ab["mhc_post_bwd"]
+        assert kb("hc_post_bwd_generic<N, IO, false>") == ab["mhc_post_bwd_nodx"]
+        e = 2 if io == "bf16" else 4
+        # dx pass, coefficient pass and dφ sum: x, dh, dx, dH, φ and bias in; dx, dφ and dbias out
+        dx_part = kb("bwd_dx_kernel<false>") + kb("dphi_bias_sum_kernel") + kb("bwd_coef_kernel")
+        assert dx_part == ab["mhc_pre_bwd"]
+        assert kb("bwd_dx_kernel<true>") - kb("bwd_dx_kernel<false>") == T * N * N * 4
+        assert kb("bwd_proj_kernel<10>") == T * (K * e + D * e) + phi
+        assert kb("phi_pack_tile_kernel") == 2 * phi
+        assert kb("no_such_kernel") is None
