@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MHC_ABI_VERSION 4
+#define MHC_ABI_VERSION 5
 
 typedef enum mhc_dtype { MHC_F32 = 0, MHC_BF16 = 1 } mhc_dtype;
 
@@ -64,7 +64,8 @@ typedef enum mhc_status {
   MHC_OK = 0,
   MHC_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, workspace too small */
   MHC_ERR_UNSUPPORTED = 2, /* N not in {1,2,4,8}, D not a multiple of 8, too many rounds */
-  MHC_ERR_HIP = 3          /* the HIP runtime rejected a launch */
+  MHC_ERR_HIP = 3,         /* the HIP runtime rejected a launch */
+  MHC_ERR_TOO_LARGE = 4    /* mhc_pre_noalloc: the call needs more than MHC_NOALLOC_SCRATCH_BYTES */
 } mhc_status;
 
 /* Problem descriptor.  T = tokens (batch × sequence), N streams, D hidden size
@@ -215,6 +216,27 @@ mhc_status mhc_post_stable_bwd(const mhc_desc* desc, const void* dx_next, const 
                                const float* out_weight, void* dx, void* dy, float* dy_weight,
                                float* dout_weight, float* dH_post, float* dH_res, void* workspace,
                                size_t workspace_bytes, hipStream_t stream);
+
+/* Size of the static scratch buffer behind mhc_pre_noalloc, in bytes: one
+ * such buffer per GPU the library runs on, held until the process ends. */
+#define MHC_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* mhc_pre for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * workspace mhc_pre takes from its caller is the library's static scratch
+ * buffer of the current device instead, and the call makes no allocation of
+ * any kind.  Arguments, layouts, results (bit for bit) and errors as for
+ * mhc_pre; in addition MHC_ERR_TOO_LARGE, with nothing launched, when
+ * mhc_pre_workspace_bytes(desc) exceeds MHC_NOALLOC_SCRATCH_BYTES (on a
+ * 256-CU MI355X every T up to 9,216 fits for bf16, N = 4, D = 5120, and up
+ * to 19,712 for D = 2560; the other paths need at most 2 MB).  The first call on a
+ * device looks up the buffer's device address (MHC_ERR_HIP if that fails).
+ * Every call on one GPU shares that GPU's buffer, which keeps the last
+ * call's contents (nothing in it needs clearing): calls on one stream are
+ * safe, calls that overlap in time on one GPU (two streams, two host threads)
+ * race and must not be made. */
+mhc_status mhc_pre_noalloc(const mhc_desc* desc, const void* x, const float* phi, const float* bias,
+                           void* h, float* H_pre, float* H_post, float* H_res, hipStream_t stream);
 
 /* MHC_ABI_VERSION of the built library. */
 int mhc_abi_version(void);

@@ -22,7 +22,7 @@ ABI_RUN = os.path.join(os.path.dirname(HERE), "tests", "c", "_build", "mhc_abi_r
 
 SOURCES = ["mhc_api.cpp", "hc_pre.hip", "hc_pre_mfma.hip", "hc_post.hip", "hc_bwd.hip",
            "hc_pre_bwd_mfma.hip", "hc_pre_decode.hip",
-           "hc_post_stable.hip", "hc_pre_tile.hip"]
+           "hc_post_stable.hip", "hc_pre_tile.hip", "mhc_noalloc.hip"]
 
 ARCH = "gfx950"
 # Packed-fp32 VALU instructions are switched off for every device pass.

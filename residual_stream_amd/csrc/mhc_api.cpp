@@ -107,6 +107,7 @@ const char* mhc_status_string(mhc_status s) {
     case MHC_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad size or scalar, workspace too small, aliasing)";
     case MHC_ERR_UNSUPPORTED: return "unsupported shape (N must be 1, 2, 4 or 8; D a multiple of 8; iteration limit)";
     case MHC_ERR_HIP: return "HIP runtime error while launching";
+    case MHC_ERR_TOO_LARGE: return "the call needs more scratch than MHC_NOALLOC_SCRATCH_BYTES (use mhc_pre with a workspace)";
   }
   return "unknown status";
 }

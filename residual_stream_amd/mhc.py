@@ -23,6 +23,7 @@ MHC_OK = 0
 MHC_ERR_INVALID_ARG = 1
 MHC_ERR_UNSUPPORTED = 2
 MHC_ERR_HIP = 3
+MHC_ERR_TOO_LARGE = 4
 
 ABI_FUNCTIONS = (
     "mhc_pre_workspace_bytes",
@@ -37,6 +38,7 @@ ABI_FUNCTIONS = (
     "mhc_post_stable",
     "mhc_post_stable_bwd_workspace_bytes",
     "mhc_post_stable_bwd",
+    "mhc_pre_noalloc",
     "mhc_status_string",
     "mhc_abi_version",
     "mhc_trace_kernel_events",
@@ -104,6 +106,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.mhc_post_stable_bwd_workspace_bytes.argtypes = [_DP, ctypes.c_int, ctypes.c_int]
     lib.mhc_post_stable_bwd.restype = ctypes.c_int
     lib.mhc_post_stable_bwd.argtypes = [_DP] + [_P] * 14 + [ctypes.c_size_t, _P]
+    lib.mhc_pre_noalloc.restype = ctypes.c_int
+    lib.mhc_pre_noalloc.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.mhc_trace_kernel_events.restype = ctypes.c_int
     lib.mhc_trace_kernel_events.argtypes = [_P, _P, ctypes.c_int, _P]
     if path is None:
@@ -251,6 +255,39 @@ def mhc_pre(x, phi, bias, *, iters=20, eps=1e-6, alphas=(0.01, 0.01, 0.01), out=
     st = lib.mhc_pre(ctypes.byref(d), _ptr(x), _ptr(_f32(phi)), _ptr(_f32(bias)), _ptr(h), _ptr(Hp),
                      _ptr(Hq), _ptr(Hr), _ptr(workspace), nbytes, _stream(stream))
     _check(st, "mhc_pre")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # MHC_NOALLOC_SCRATCH_BYTES of include/mhc.h
+
+
+def mhc_pre_noalloc(x, phi, bias, *, iters=20, eps=1e-6, alphas=(0.01, 0.01, 0.01), out=None, stream=None):
+    """hc_pre on the library's static scratch buffer (``mhc_pre_noalloc``):
+    no workspace, and with ``out`` given no allocation at all.  Results equal
+    :func:`mhc_pre`'s bit for bit; raises MhcError with status
+    MHC_ERR_TOO_LARGE where the call needs more than the buffer holds.  Calls
+    that overlap in time on one GPU race on its buffer.
+
+    Returns (h[T,D], H_pre[T,N], H_post[T,N], H_res[T,N,N])."""
+    lib = load()
+    T, N, D, io, dv = _state(x)
+    d = desc_for(x, iters, eps, alphas)
+    sh = _coef_shapes(T, N, D)
+    _expect("phi", phi, sh["phi"], torch.float32, dv)
+    _expect("bias", bias, sh["bias"], torch.float32, dv)
+    if out is None:
+        out = (torch.empty((T, D), dtype=x.dtype, device=x.device),
+               torch.empty((T, N), dtype=torch.float32, device=x.device),
+               torch.empty((T, N), dtype=torch.float32, device=x.device),
+               torch.empty((T, N, N), dtype=torch.float32, device=x.device))
+    h, Hp, Hq, Hr = out
+    _expect("h", h, (T, D), io, dv)
+    _expect("H_pre", Hp, sh["H"], torch.float32, dv)
+    _expect("H_post", Hq, sh["H"], torch.float32, dv)
+    _expect("H_res", Hr, sh["H_res"], torch.float32, dv)
+    st = lib.mhc_pre_noalloc(ctypes.byref(d), _ptr(x), _ptr(_f32(phi)), _ptr(_f32(bias)), _ptr(h), _ptr(Hp),
+                             _ptr(Hq), _ptr(Hr), _stream(stream))
+    _check(st, "mhc_pre_noalloc")
     return out
 
 
