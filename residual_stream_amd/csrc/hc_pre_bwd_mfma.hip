@@ -6,8 +6,9 @@
 // paragraph).  Three passes:
 //
 //  1. bwd_proj_kernel — split-K reduction.  A persistent workgroup keeps one
-//     d-slice of φ (all four streams) in registers as bf16 and streams x and
-//     dh for a contiguous token range: per (token, slice) it writes the raw
+//     d-slice of φ (all four streams) in registers as bf16 high and low parts
+//     (φ = hi + lo: x is exact in bf16, so x·hi + x·lo keeps fp32 accuracy)
+//     and streams x and dh for a contiguous token range: per (token, slice) it writes the raw
 //     projections x·φ (matrix cores), the sum of squares and <dh, x[n]>.
 //  2. bwd_coef_kernel — per token, four lanes (one per H_res row): sums the
 //     slices, recomputes rstd, logits, gates and the Sinkhorn rounds (keeping
@@ -15,8 +16,11 @@
 //     backwards and emits G = rstd·α⊙dℓ (the token's factor in dφ and in
 //     dx̄ = G·φᵀ), β = rstd³·(dq·p)/K, H_pre, dℓ and the dα terms.
 //  3. bwd_dx_kernel — per k-slice: dx += G·φᵀ − β·x + H_pre[n]·dh (matrix
-//     cores, φ slice in LDS) and the partial dφ = Σ_t x_tᵀ G_t over its token
-//     range (matrix cores on an LDS-transposed copy of the x tile).
+//     cores, φ slice in registers) and the partial dφ = Σ_t x_tᵀ G_t over its
+//     token range (matrix cores on an LDS-transposed copy of the x tile); G
+//     enters the matrix cores as bf16 high and low parts, so dφ keeps fp32
+//     accuracy; φ enters G·φᵀ rounded to bf16 (an error of the order of the
+//     bf16 rounding of the dx that product is added to).
 // A final kernel sums the dφ partials and the per-16-token dbias / dα rows
 // (fixed orders).
 #include "mhc_coef.h"
@@ -70,7 +74,11 @@ __device__ __forceinline__ f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
 // squares and <dh, x[n]> go to v_dot2_f32_bf16.  The waves' partials meet in
 // LDS and one summed record per (slice, token) goes to the workspace, a block
 // late (after the next block's barrier): one barrier per block.
-constexpr int kPRing = 4;  // register slots of x/dh pieces per thread (a fifth spills at W = 10)
+// register slots of x/dh pieces per thread: three blocks in flight at W = 8,
+// two at W = 10 (whose 640 threads keep as many bytes in flight; a fourth
+// slot there spills next to φ's high and low fragments)
+template <int W>
+constexpr int kPRing = W == 10 ? 3 : 4;
 
 // f(integral_constant<int, i>) for i = I .. N − 1, in order.
 template <int I, int N, typename F>
@@ -136,7 +144,8 @@ __global__ __launch_bounds__(64 * W, 1) void bwd_proj_kernel(
   const uint32_t gh = (uint32_t)((htk * D + slice * kSl + 8 * hc) * 2);
   const uint32_t lh = (uint32_t)(16 * TL::kXRow + htk * TL::kHRow + hc * 16);
 
-  uint4 xs[kPRing][4], hs[kPRing];
+  constexpr int kRing = kPRing<W>;
+  uint4 xs[kRing][4], hs[kRing];
   auto load_blk = [&](int b, auto slot_c) {
     constexpr int SL = decltype(slot_c)::value;
     const int t0 = tb + 16 * b;
@@ -150,11 +159,13 @@ __global__ __launch_bounds__(64 * W, 1) void bwd_proj_kernel(
   };
 
   // φ: stream by stream through LDS (the red buffer).  Its global loads go out
-  // first, then those of the first kPRing − 1 blocks, so that x and dh stream
+  // first, then those of the first kRing − 1 blocks, so that x and dh stream
   // while φ is staged: a CU's vector-memory path is the bottleneck here, and
   // φ queued behind three blocks of x and dh would hold up the first block by
   // their transfer time.
-  uint4 bfr[kN][2];
+  // φ as two bf16 parts, φ = hi + lo (x is exact in bf16, so x·hi + x·lo
+  // keeps about 16 mantissa bits of φ in the fp32 accumulation)
+  uint4 bfr[kN][2], bfl[kN][2];
   {
     constexpr int kV4 = kSl * kC / 4;  // float4 of one stream's slice rows
     constexpr int kPer = (kV4 + kThr - 1) / kThr;
@@ -169,7 +180,7 @@ __global__ __launch_bounds__(64 * W, 1) void bwd_proj_kernel(
       }
     __builtin_amdgcn_sched_barrier(0);
     // (kept in issue order: the wait counts in the loop assume slot 0 oldest)
-    unroll_slots<0, kPRing - 1>([&](auto sl) {
+    unroll_slots<0, kRing - 1>([&](auto sl) {
       load_blk(decltype(sl)::value, sl);
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -191,6 +202,7 @@ __global__ __launch_bounds__(64 * W, 1) void bwd_proj_kernel(
         for (int v = 0; v < 8; ++v) v8[v] = c < kC ? stage[(wave * 32 + 8 * g + v) * kC + c] : 0.f;
         bfr[n][cg] = make_uint4(pack_bf16x2(v8[0], v8[1]), pack_bf16x2(v8[2], v8[3]),
                                 pack_bf16x2(v8[4], v8[5]), pack_bf16x2(v8[6], v8[7]));
+        bfl[n][cg] = pack_bf16x8_rest(v8, bfr[n][cg]);
       }
       __syncthreads();
     }
@@ -215,7 +227,7 @@ __global__ __launch_bounds__(64 * W, 1) void bwd_proj_kernel(
 
   auto block = [&](int b, auto slot_c) {
     constexpr int SL = decltype(slot_c)::value;
-    load_blk(b + kPRing - 1, std::integral_constant<int, (SL + kPRing - 1) % kPRing>{});
+    load_blk(b + kRing - 1, std::integral_constant<int, (SL + kRing - 1) % kRing>{});
     __builtin_amdgcn_sched_barrier(0);
     char* tl = tile[b & 1];
 #pragma unroll
@@ -231,6 +243,8 @@ __global__ __launch_bounds__(64 * W, 1) void bwd_proj_kernel(
       const uint4 a = *reinterpret_cast<const uint4*>(tl + row * TL::kXRow + (n * kCh + 4 * wave + g) * 16);
       acc0 = mfma(a, bfr[n][0], acc0);
       acc1 = mfma(a, bfr[n][1], acc1);
+      acc0 = mfma(a, bfl[n][0], acc0);
+      acc1 = mfma(a, bfl[n][1], acc1);
       ss = dot2(a.x, a.x, ss);
       ss = dot2(a.y, a.y, ss);
       ss = dot2(a.z, a.z, ss);
@@ -266,7 +280,7 @@ __global__ __launch_bounds__(64 * W, 1) void bwd_proj_kernel(
   // loop with a single exit keeps each slot in the same registers on every
   // pass, so the wait counts stay exact across the back edge.
   int b = 0;
-  for (; b < nblk; b += kPRing) unroll_slots<0, kPRing>([&](auto sl) { block(b + decltype(sl)::value, sl); });
+  for (; b < nblk; b += kRing) unroll_slots<0, kRing>([&](auto sl) { block(b + decltype(sl)::value, sl); });
   if (b > 0) {
     __syncthreads();
     record(b - 1);
@@ -473,10 +487,11 @@ __global__ __launch_bounds__(kCoefThreads) void bwd_coef_kernel(
 // wave access covers whole 128-byte lines.  The matrix-core work meets that
 // layout in LDS:
 //  * dx̄ = G·φᵀ: wave w owns stream w's 128 d (eight 16-row k blocks), A = its
-//    φ rows (bf16, in VGPRs for the whole kernel), B = the tile's G; results
-//    to LDS as [t][k];
+//    φ rows (bf16, in VGPRs for the whole kernel), B = the tile's G (bf16
+//    high and low parts); results to LDS as [t][k];
 //  * dφ += xᵀ·G over the tile's 16 tokens: the same k blocks × two column
-//    blocks, A = xᵀ gathered from the LDS copy of the x tile, B = Gᵀ.
+//    blocks, A = xᵀ gathered from the LDS copy of the x tile, B = Gᵀ (both
+//    parts).
 // Each thread then finishes its pieces: dx += dx̄ − β·x + H_pre[n]·dh.
 // The next tile's x, dx, dh and coefficients are loaded while a tile is
 // worked on (two register buffers; vector memory completes in order, so those
@@ -510,8 +525,8 @@ __global__ __launch_bounds__(kDxThreads, 2) void bwd_dx_kernel(
     const float* __restrict__ hres) {
   __shared__ __align__(16) uint16_t xs[kDxTile * kXRow];     // x[t][k] of the tile
   __shared__ __align__(16) float dxr[kDxTile * kRRow];       // (G·φᵀ)[t][k]
-  __shared__ __align__(16) uint16_t Gs[kDxTile * kGRow];     // G[t][c]
-  __shared__ __align__(16) uint16_t GTs[32 * kTRow];         // Gᵀ[c][t]
+  __shared__ __align__(16) uint16_t Gs[2][kDxTile * kGRow];  // G[t][c]: bf16 high, low parts
+  __shared__ __align__(16) uint16_t GTs[2][32 * kTRow];      // Gᵀ[c][t]: the same two parts
   __shared__ __align__(16) uint16_t hs[2][kDxTile * kHRow];  // dh[t][d], by tile parity
   __shared__ float bs[2][kDxTile];                           // β, by tile parity
   __shared__ __align__(16) float hps[2][kDxTile][kN];        // H_pre, by tile parity
@@ -527,7 +542,7 @@ __global__ __launch_bounds__(kDxThreads, 2) void bwd_dx_kernel(
   const int row = lane & 15, g = lane >> 4;
 
   // φ A fragments of this wave: rows k = stream w, d_base + 16·kb + row;
-  // columns c = 8g .. 8g+7 (g = 3: c ≥ 24, zero)
+  // columns c = 8g .. 8g+7 (g = 3: c ≥ 24, zero), rounded to bf16
   uint4 af[8];
   {
     float4 f[8][2];
@@ -616,12 +631,19 @@ __global__ __launch_bounds__(kDxThreads, 2) void bwd_dx_kernel(
     {
       const float4 v = bc[SL];
       if (tid < 128) {
-        const uint32_t lo = pack_bf16x2(v.x, v.y), hi = pack_bf16x2(v.z, v.w);
-        *reinterpret_cast<uint2*>(&Gs[ct * kGRow + cc]) = make_uint2(lo, hi);
-        GTs[(cc + 0) * kTRow + ct] = (uint16_t)(lo & 0xffffu);
-        GTs[(cc + 1) * kTRow + ct] = (uint16_t)(lo >> 16);
-        GTs[(cc + 2) * kTRow + ct] = (uint16_t)(hi & 0xffffu);
-        GTs[(cc + 3) * kTRow + ct] = (uint16_t)(hi >> 16);
+        // G as bf16 high and low parts, G = hi + lo
+        const uint32_t w0 = pack_bf16x2(v.x, v.y), w1 = pack_bf16x2(v.z, v.w);
+        const uint32_t r0 = pack_bf16x2_rest(v.x, v.y, w0), r1 = pack_bf16x2_rest(v.z, v.w, w1);
+        *reinterpret_cast<uint2*>(&Gs[0][ct * kGRow + cc]) = make_uint2(w0, w1);
+        *reinterpret_cast<uint2*>(&Gs[1][ct * kGRow + cc]) = make_uint2(r0, r1);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const uint32_t a = p ? r0 : w0, b = p ? r1 : w1;
+          GTs[p][(cc + 0) * kTRow + ct] = (uint16_t)(a & 0xffffu);
+          GTs[p][(cc + 1) * kTRow + ct] = (uint16_t)(a >> 16);
+          GTs[p][(cc + 2) * kTRow + ct] = (uint16_t)(b & 0xffffu);
+          GTs[p][(cc + 3) * kTRow + ct] = (uint16_t)(b >> 16);
+        }
       } else if (tid < 144) {
         bs[SL][ct] = v.x;
         hps[SL][ct][0] = v.y;
@@ -639,61 +661,38 @@ __global__ __launch_bounds__(kDxThreads, 2) void bwd_dx_kernel(
     __syncthreads();
     // ---- matrix cores
     {
-      const uint4 gb = *reinterpret_cast<const uint4*>(&Gs[row * kGRow + 8 * g]);  // B: Gᵀ[c][t]
+      // B: Gᵀ[c][t], high and low parts (φ enters as its bf16 rounding: the
+      // error that leaves in G·φᵀ is of the order of the bf16 rounding of
+      // the dx it is added to)
+      const uint4 gb = *reinterpret_cast<const uint4*>(&Gs[0][row * kGRow + 8 * g]);
+      const uint4 gbl = *reinterpret_cast<const uint4*>(&Gs[1][row * kGRow + 8 * g]);
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb) {
-        const f32x4_t r = mfma(af[kb], gb, f32x4_t{0.f, 0.f, 0.f, 0.f});
+        f32x4_t r = mfma(af[kb], gb, f32x4_t{0.f, 0.f, 0.f, 0.f});
+        r = mfma(af[kb], gbl, r);
         *reinterpret_cast<f32x4_t*>(&dxr[row * kRRow + wave * kDxWd + 16 * kb + 4 * g]) = r;
       }
-      s16x4_t gt[2];
+      s16x4_t gt[2][2];
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-        gt[cb] = *reinterpret_cast<const s16x4_t*>(&GTs[(16 * cb + row) * kTRow + 4 * g]);
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+          gt[p][cb] = *reinterpret_cast<const s16x4_t*>(&GTs[p][(16 * cb + row) * kTRow + 4 * g]);
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb) {
         const int k = wave * kDxWd + 16 * kb + row;
         const s16x4_t a = {(short)xs[(4 * g + 0) * kXRow + k], (short)xs[(4 * g + 1) * kXRow + k],
                            (short)xs[(4 * g + 2) * kXRow + k], (short)xs[(4 * g + 3) * kXRow + k]};
-        dacc[kb][0] = mfma16(a, gt[0], dacc[kb][0]);
-        dacc[kb][1] = mfma16(a, gt[1], dacc[kb][1]);
+        dacc[kb][0] = mfma16(a, gt[0][0], dacc[kb][0]);
+        dacc[kb][1] = mfma16(a, gt[0][1], dacc[kb][1]);
+        dacc[kb][0] = mfma16(a, gt[1][0], dacc[kb][0]);
+        dacc[kb][1] = mfma16(a, gt[1][1], dacc[kb][1]);
       }
     }
     __syncthreads();
     // ---- finish this thread's pieces
     const uint32_t rows = rows_in(t0);
     const auto ro = make_rsrc(dx + (rows > 0 ? t0 : 0) * K, rows * (uint32_t)K * 2);
-    // MIX: the token's hc_post part, dx[m] = Σ_n H_res[n][m]·dx_next[n] in
-    // the arithmetic of mhc_post_bwd (fused multiply-adds over n from zero,
-    // rounded to bf16), for the four streams m this thread holds
-    uint4 mixed[4];
-    if constexpr (MIX) {
-      const int t = tid >> 4;
-      float hr[kN][kN];
-#pragma unroll
-      for (int n = 0; n < kN; ++n) {
-        const float4 r = *reinterpret_cast<const float4*>(&hrs[SL][t][n * kN]);
-        hr[n][0] = r.x;
-        hr[n][1] = r.y;
-        hr[n][2] = r.z;
-        hr[n][3] = r.w;
-      }
-#pragma unroll
-      for (int m = 0; m < kN; ++m) {
-        uint32_t w[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-          for (int n = 0; n < kN; ++n) {
-            const uint32_t g = (&bd[SL][n].x)[q];
-            a0 += hr[n][m] * bf16_lo(g);
-            a1 += hr[n][m] * bf16_hi(g);
-          }
-          w[q] = pack_bf16x2(a0, a1);
-        }
-        mixed[m] = make_uint4(w[0], w[1], w[2], w[3]);
-      }
-    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int t = ptok(j), sn = pstr(j);
@@ -703,7 +702,31 @@ __global__ __launch_bounds__(kDxThreads, 2) void bwd_dx_kernel(
       const uint4 hv = *reinterpret_cast<const uint4*>(&hs[SL][t * kHRow + 8 * pc]);
       const float beta = bs[SL][t], hp = hps[SL][t][sn];
       const float rv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-      const uint4 xv = bx[SL][j], dv = MIX ? mixed[j] : bd[SL][j];
+      uint4 dv;
+      if constexpr (MIX) {
+        // the token's hc_post part for stream j, Σ_n H_res[n][j]·dx_next[n], in
+        // the arithmetic of mhc_post_bwd (fused multiply-adds over n from
+        // zero, rounded to bf16); formed piece by piece to keep registers free
+        float hc[kN];
+#pragma unroll
+        for (int n = 0; n < kN; ++n) hc[n] = hrs[SL][t][n * kN + j];
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+          for (int n = 0; n < kN; ++n) {
+            const uint32_t gw = (&bd[SL][n].x)[q];
+            a0 += hc[n] * bf16_lo(gw);
+            a1 += hc[n] * bf16_hi(gw);
+          }
+          w[q] = pack_bf16x2(a0, a1);
+        }
+        dv = make_uint4(w[0], w[1], w[2], w[3]);
+      } else {
+        dv = bd[SL][j];
+      }
+      const uint4 xv = bx[SL][j];
       const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, hw[4] = {hv.x, hv.y, hv.z, hv.w},
                      dw[4] = {dv.x, dv.y, dv.z, dv.w};
       float base[8];

@@ -38,6 +38,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
+// The parts of (lo, hi) that their bf16 pair w = pack_bf16x2(lo, hi) leaves
+// out, rounded to bf16 in turn: with it, a value is carried as two bf16
+// parts whose sum keeps about 16 mantissa bits.
+__device__ __forceinline__ uint32_t pack_bf16x2_rest(float lo, float hi, uint32_t w) {
+  return pack_bf16x2(lo - bf16_lo(w), hi - bf16_hi(w));
+}
+__device__ __forceinline__ uint4 pack_bf16x8_rest(const float v[8], uint4 w) {
+  return make_uint4(pack_bf16x2_rest(v[0], v[1], w.x), pack_bf16x2_rest(v[2], v[3], w.y),
+                    pack_bf16x2_rest(v[4], v[5], w.z), pack_bf16x2_rest(v[6], v[7], w.w));
+}
 
 // Eight consecutive elements starting at element index `i` (i % 8 == 0,
 // 16-byte aligned base), widened to fp32.

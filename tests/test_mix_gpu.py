@@ -17,7 +17,7 @@ import torch
 from residual_stream_amd import mhc
 from residual_stream_amd.inputs import make_inputs
 
-from mhc_testlib import TOL, assert_close, dev, gpu_forward, host, oracle_backward
+from mhc_testlib import TOL, assert_close, tol_of, dev, gpu_forward, host, oracle_backward
 
 pytestmark = pytest.mark.gpu
 
@@ -67,10 +67,8 @@ def test_mix_matches_oracle_and_the_two_calls(io, N, D, T, fused):
         assert torch.equal(a, b), name
     # the total state gradient against the oracle
     ref = oracle_backward(inp)
-    tol = TOL[io]
-    assert_close("dx", host(mix[0]), ref["dx"], tol)
-    assert_close("dphi", host(mix[1]), ref["dphi"], tol)
-    assert_close("dbias", host(mix[2]), ref["dbias"], tol)
+    for name, got in (("dx", mix[0]), ("dphi", mix[1]), ("dbias", mix[2])):
+        assert_close(name, host(got), ref[name], tol_of(name, io))
     assert torch.equal(_bits(mix[0]), _bits(two[0])), f"dx differs from the two calls (fused={fused})"
 
 

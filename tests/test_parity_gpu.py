@@ -15,7 +15,7 @@ import torch
 from residual_stream_amd import mhc
 from residual_stream_amd.inputs import make_inputs
 
-from mhc_testlib import (TOL, assert_close, dev, gpu_backward, gpu_forward, host,
+from mhc_testlib import (assert_close, tol_of, dev, gpu_backward, gpu_forward, host,
                          oracle_backward, oracle_forward)
 
 pytestmark = pytest.mark.gpu
@@ -42,7 +42,7 @@ def check_forward(inp, tokens=None):
         got = host(g[k])
         if tokens is not None:
             got = got[tokens]
-        errs[k] = assert_close(k, got, r[k], TOL[inp.io])
+        errs[k] = assert_close(k, got, r[k], tol_of(k, inp.io))
     return errs
 
 
@@ -56,7 +56,7 @@ def check_backward(inp, tokens=None):
         got, ref = host(g[k]), r[k]
         if tokens is not None and k not in ("dphi", "dbias", "dalpha"):
             got, ref = got[tokens], ref[tokens]
-        errs[k] = assert_close(k, got, ref, TOL[inp.io])
+        errs[k] = assert_close(k, got, ref, tol_of(k, inp.io))
     return errs
 
 

@@ -15,7 +15,7 @@ from oracle import mhc_oracle as O
 from residual_stream_amd import mhc
 from residual_stream_amd.inputs import make_coefficients, make_inputs, to_io
 
-from mhc_testlib import TOL, assert_close, dev, host
+from mhc_testlib import assert_close, dev, host, tol_of
 
 pytestmark = pytest.mark.gpu
 
@@ -77,17 +77,14 @@ def test_fused_matches_oracle(io, T, D):
     kw = dict(iters=b.iters, eps=b.eps, alphas=b.alphas)
     xn, h, Hp2, Hq2, Hr2 = mhc.mhc_post_pre(x, y, Hq, Hr, dev(b.phi), dev(b.bias), **kw)
     torch.cuda.synchronize()
-    tol = TOL[io]
     Hq_ref, Hr_ref = make_coefficients(T, 4, seed=21 + 2000)
     ref_xn = O.hc_post(a.x, a.y, Hq_ref, Hr_ref)
-    assert_close("x_next", host(xn), ref_xn, tol)
+    assert_close("x_next", host(xn), ref_xn, tol_of("x_next", io))
     # the next layer reads x_next as stored (rounded to the I/O dtype)
     xn_io = to_io(ref_xn.astype(np.float32), io).astype(np.float64)
     ref = O.hc_pre(xn_io, b.phi, b.bias, b.alphas, b.eps, b.iters)
-    assert_close("h", host(h), ref["h"], tol)
-    assert_close("H_pre", host(Hp2), ref["H_pre"], tol)
-    assert_close("H_post", host(Hq2), ref["H_post"], tol)
-    assert_close("H_res", host(Hr2), ref["H_res"], tol)
+    for name, got in (("h", h), ("H_pre", Hp2), ("H_post", Hq2), ("H_res", Hr2)):
+        assert_close(name, host(got), ref[name], tol_of(name, io))
 
 
 def test_fused_full_size_equals_post_then_pre():

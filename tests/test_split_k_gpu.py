@@ -32,7 +32,7 @@ from oracle import mhc_oracle as O
 from residual_stream_amd import mhc
 from residual_stream_amd.inputs import make_coefficients, make_inputs, to_io
 
-from mhc_testlib import (TOL, assert_close, dev, gpu_backward, gpu_forward, host,
+from mhc_testlib import (TOL, assert_close, tol_of, dev, gpu_backward, gpu_forward, host,
                          oracle_backward, oracle_forward)
 
 pytestmark = pytest.mark.gpu
@@ -105,7 +105,7 @@ def check_forward(inp, tokens=None, tag=""):
         got = host(g[k])
         if tokens is not None:
             got = got[tokens]
-        assert_close(k, got, r[k], TOL[inp.io], case=f"{tag} T={inp.T} D={inp.D}")
+        assert_close(k, got, r[k], tol_of(k, inp.io), case=f"{tag} T={inp.T} D={inp.D}")
 
 
 # -------------------------------------------- split-K forward, alpha = 1 ---
@@ -150,7 +150,7 @@ def test_fused_post_pre_alpha1_full_size(T, D):
     xn_io = to_io(ref_xn.astype(np.float32), "bf16").astype(np.float64)
     ref = O.hc_pre(xn_io, b.phi, b.bias, b.alphas, b.eps, b.iters)
     for name, got in (("h", h), ("H_pre", Hp), ("H_post", Hq), ("H_res", Hr)):
-        assert_close(name, host(got)[tk], ref[name], TOL["bf16"], case=case)
+        assert_close(name, host(got)[tk], ref[name], tol_of(name, "bf16"), case=case)
 
 
 # ----------------------------------------- tiled backward, alpha = 1 ---
@@ -176,7 +176,7 @@ def check_backward(inp, tokens=None, tag=""):
         got, ref = host(g[k]), r[k]
         if tokens is not None and k not in ("dphi", "dbias", "dalpha"):
             got, ref = got[tokens], ref[tokens]
-        assert_close(k, got, ref, TOL[inp.io], case=f"{tag} T={inp.T} D={inp.D}")
+        assert_close(k, got, ref, tol_of(k, inp.io), case=f"{tag} T={inp.T} D={inp.D}")
 
 
 def test_tiled_backward_alpha1_full_size_bf16():

@@ -19,7 +19,7 @@ from oracle import mhc_oracle as O
 from residual_stream_amd import mhc
 from residual_stream_amd.inputs import make_inputs
 
-from mhc_testlib import TOL, assert_close, dev, host
+from mhc_testlib import assert_close, dev, host, tol_of
 
 pytestmark = pytest.mark.gpu
 
@@ -60,7 +60,7 @@ def test_noalloc_equals_mhc_pre_call_after_call():
         if k == 1:  # and the oracle, on every token of this one
             r = O.hc_pre(inp.x, inp.phi, inp.bias, inp.alphas, inp.eps, inp.iters)
             for name, a in zip(NAMES, got):
-                assert_close(name, host(a), r[name], TOL[io], case=f"noalloc T={T} D={D}")
+                assert_close(name, host(a), r[name], tol_of(name, io), case=f"noalloc T={T} D={D}")
 
 
 def test_noalloc_refuses_calls_beyond_its_buffer():
