@@ -10,7 +10,7 @@
 //     (φ = hi + lo: x is exact in bf16, so x·hi + x·lo keeps fp32 accuracy)
 //     and streams x and dh for a contiguous token range: per (token, slice) it writes the raw
 //     projections x·φ (matrix cores), the sum of squares and <dh, x[n]>.
-//  2. bwd_coef_kernel — per token, four lanes (one per H_res row): sums the
+//  2. bwd_coef_kernel — per token, sixteen lanes (one per H_res entry): sums the
 //     slices, recomputes rstd, logits, gates and the Sinkhorn rounds (keeping
 //     the row/column scalings u, v of every round in LDS), walks the rounds
 //     backwards and emits G = rstd·α⊙dℓ (the token's factor in dφ and in
@@ -289,15 +289,25 @@ __global__ __launch_bounds__(64 * W, 1) void bwd_proj_kernel(
 
 // ------------------------------------------------------------- pass 2 ---
 // Per-token outputs, fp32: coef[t][64] = G[0..31] (c ≥ 24 zero), β at 32,
-// H_pre[33..36]; dlog[t][24]; dal[t][4].
+// H_pre[33..36]; dlog[r][24] and dal[r][4], one row per four tokens.
+// A wave takes four tokens, one H_res entry per lane (lane 16·tk + 4·i + j:
+// token tk, row i, column j), so the Sinkhorn rounds and their reverse walk
+// are a few instructions per lane each: sums along a row of H_res over the
+// lane quad, along a column over the rotations by 4 and 8 of the 16-lane DPP
+// row.  The pass has no HBM volume to speak of; its time is the latency of
+// those chains, which four times as many lanes per token shorten.
 constexpr int kCoefStride = 64;
-constexpr int kCoefThreads = 64;  // 16 tokens × 4 rows
+constexpr int kCoefThreads = 64;
+constexpr int kCoefTokens = 4;  // tokens per workgroup (and per dlog / dal row)
 
-constexpr int kQuadXor1 = 0xB1;
-constexpr int kQuadXor2 = 0x4E;
-__device__ __forceinline__ float quad_sum(float v) {
-  v += dpp<kQuadXor1>(v);
-  v += dpp<kQuadXor2>(v);
+__device__ __forceinline__ float row_sum4(float v) {  // Σ_j of entry (i, j)
+  v += dpp<0xB1>(v);  // quad_perm(1,0,3,2)
+  v += dpp<0x4E>(v);  // quad_perm(2,3,0,1)
+  return v;
+}
+__device__ __forceinline__ float col_sum4(float v) {  // Σ_i of entry (i, j)
+  v += dpp<0x124>(v);  // row_ror:4
+  v += dpp<0x128>(v);  // row_ror:8
   return v;
 }
 __global__ __launch_bounds__(kCoefThreads) void bwd_coef_kernel(
@@ -310,171 +320,121 @@ __global__ __launch_bounds__(kCoefThreads) void bwd_coef_kernel(
     a_post = alpha_dev[1];
     a_res = alpha_dev[2];
   }
-  extern __shared__ float hist[];  // per lane and round: u_i, then v_i (v_j read from lane j)
+  extern __shared__ float hist[];  // per lane and round: u_i, then v_j
   const int lane = threadIdx.x;
-  const int i = lane & 3;                 // H_res row owned by this lane
-  const int64_t t = (int64_t)blockIdx.x * 16 + (lane >> 2);
+  const int e = lane & 15, i = e >> 2, j = e & 3;
+  const int64_t t = (int64_t)blockIdx.x * kCoefTokens + (lane >> 4);
   const bool tok = t < T;
   const int64_t tc = tok ? t : T - 1;
   const int K = kN * D;
 
-  // slice sums (fixed order) of this row's columns: pre i, post i, res row i, ss, dhp i
-  float p_pre = 0.f, p_post = 0.f, p_res[kN] = {0.f, 0.f, 0.f, 0.f}, ss = 0.f, dhp = 0.f;
-  // eight slices' loads in flight at once (one memory round trip per eight
-  // slices instead of one per slice); slices past the count read slice 0 and
+  // slice sums (fixed order): pre i, post i, res (i, j), ss, dhp i.  Eight
+  // slices' loads in flight at once; slices past the count read slice 0 and
   // add nothing, so the sums keep the slice order
+  float p_pre = 0.f, p_post = 0.f, p_res = 0.f, ss = 0.f, dhp = 0.f;
   constexpr int kChunk = 8;
   for (int s0 = 0; s0 < nslices; s0 += kChunk) {
-    float4 va[kChunk], vb[kChunk];
-    float vc[kChunk], vd[kChunk], ve[kChunk];
+    float va[kChunk], vb[kChunk], vc[kChunk], vd[kChunk], ve[kChunk];
 #pragma unroll
     for (int u = 0; u < kChunk; ++u) {
       const int s = s0 + u < nslices ? s0 + u : 0;
       const float* pp = part + ((int64_t)s * T + tc) * kPartStride;
-      va[u] = *reinterpret_cast<const float4*>(pp + 2 * kN + i * kN);  // res row i
+      va[u] = pp[2 * kN + e];
       vc[u] = pp[i];
       vd[u] = pp[kN + i];
       ve[u] = pp[kC];
-      vb[u].x = pp[kC + 1 + i];
+      vb[u] = pp[kC + 1 + i];
     }
 #pragma unroll
     for (int u = 0; u < kChunk; ++u) {
       if (s0 + u < nslices) {
         p_pre += vc[u];
         p_post += vd[u];
-        p_res[0] += va[u].x;
-        p_res[1] += va[u].y;
-        p_res[2] += va[u].z;
-        p_res[3] += va[u].w;
+        p_res += va[u];
         ss += ve[u];
-        dhp += vb[u].x;
+        dhp += vb[u];
       }
     }
   }
   // same arithmetic as the forward kernels (hardware reciprocal and
-  // reciprocal square root): this pass is one wave per four CUs, so its time
-  // is the latency of these chains
+  // reciprocal square root)
   const float rstd = __builtin_amdgcn_rsqf(ss / (float)K + eps);
-  const float q_pre = rstd * p_pre, q_post = rstd * p_post;
+  const float q_pre = rstd * p_pre, q_post = rstd * p_post, q_res = rstd * p_res;
   const float l_pre = a_pre * q_pre + bias[i];
   const float l_post = a_post * q_post + bias[kN + i];
   const float s_pre = __builtin_amdgcn_rcpf(1.0f + expf(-l_pre));
   const float s_post = __builtin_amdgcn_rcpf(1.0f + expf(-l_post));
-  float q_res[kN], m0[kN], mx = -__builtin_huge_valf();
-#pragma unroll
-  for (int j = 0; j < kN; ++j) {
-    q_res[j] = rstd * p_res[j];
-    m0[j] = a_res * q_res[j] + bias[2 * kN + i * kN + j];
-    mx = fmaxf(mx, m0[j]);
-  }
-#pragma unroll
-  for (int j = 0; j < kN; ++j) m0[j] = expf(m0[j] - mx);
+  float m0 = a_res * q_res + bias[2 * kN + e];
+  float mx = fmaxf(m0, dpp<0xB1>(m0));
+  mx = fmaxf(mx, dpp<0x4E>(mx));
+  m0 = expf(m0 - mx);
 
   // forward rounds on the scalings: M = diag(u)·M0·diag(v)
-  float u = 1.f, v[kN] = {1.f, 1.f, 1.f, 1.f};
+  float u = 1.f, v = 1.f;
   float* h = hist + lane;  // stride 64 floats between entries
   for (int it = 0; it < iters; ++it) {
-    float r = 0.f;
-#pragma unroll
-    for (int j = 0; j < kN; ++j) r += m0[j] * v[j];
-    u = __builtin_amdgcn_rcpf(r);  // row i now sums to 1
-#pragma unroll
-    for (int j = 0; j < kN; ++j) {
-      const float cj = quad_sum(u * m0[j] * v[j]);  // column j sum
-      v[j] = v[j] * __builtin_amdgcn_rcpf(cj);
-    }
+    u = __builtin_amdgcn_rcpf(row_sum4(m0 * v));         // row i now sums to 1
+    v = v * __builtin_amdgcn_rcpf(col_sum4(u * m0 * v));  // column j now sums to 1
     h[(it * 2 + 0) * 64] = u;
-    h[(it * 2 + 1) * 64] = v[i];
+    h[(it * 2 + 1) * 64] = v;
   }
-  const float* hq = hist + (lane & ~3);  // v_j of this token's round: hq[(it·2+1)·64 + j]
 
   // backward: G = dL/dM, walked from the last column step to the first row step
-  float G[kN];
-#pragma unroll
-  for (int j = 0; j < kN; ++j) G[j] = tok ? dH_res[(tc * kN + i) * kN + j] : 0.f;
+  float G = tok ? dH_res[tc * kN * kN + e] : 0.f;
   for (int it = iters - 1; it >= 0; --it) {
-    const float u_s = h[(it * 2) * 64];
-    float v_s[kN], v_p[kN], u_p;
-#pragma unroll
-    for (int j = 0; j < kN; ++j) v_s[j] = hq[(it * 2 + 1) * 64 + j];
-    if (it > 0) {
-      u_p = h[((it - 1) * 2) * 64];
-#pragma unroll
-      for (int j = 0; j < kN; ++j) v_p[j] = hq[((it - 1) * 2 + 1) * 64 + j];
-    } else {
-      u_p = 1.f;
-#pragma unroll
-      for (int j = 0; j < kN; ++j) v_p[j] = 1.f;
-    }
-    // column step: X = M0·u_s·v_p, Y = M0·u_s·v_s, divisor c_j = v_p[j]/v_s[j]
-#pragma unroll
-    for (int j = 0; j < kN; ++j) {
-      const float y = m0[j] * u_s * v_s[j];
-      const float colacc = quad_sum(G[j] * y);
-      G[j] = (G[j] - colacc) * (v_s[j] * __builtin_amdgcn_rcpf(v_p[j]));
-    }
-    // row step: X = M0·u_p·v_p, Y = M0·u_s·v_p, divisor r = u_p/u_s
-    float rowacc = 0.f;
-#pragma unroll
-    for (int j = 0; j < kN; ++j) rowacc += G[j] * (m0[j] * u_s * v_p[j]);
-    const float rinv = u_s * __builtin_amdgcn_rcpf(u_p);
-#pragma unroll
-    for (int j = 0; j < kN; ++j) G[j] = (G[j] - rowacc) * rinv;
+    const float u_s = h[(it * 2) * 64], v_s = h[(it * 2 + 1) * 64];
+    const float u_p = it > 0 ? h[((it - 1) * 2) * 64] : 1.f;
+    const float v_p = it > 0 ? h[((it - 1) * 2 + 1) * 64] : 1.f;
+    // column step: X = M0·u_s·v_p, Y = M0·u_s·v_s, divisor c_j = v_p/v_s
+    const float colacc = col_sum4(G * (m0 * u_s * v_s));
+    G = (G - colacc) * (v_s * __builtin_amdgcn_rcpf(v_p));
+    // row step: X = M0·u_p·v_p, Y = M0·u_s·v_p, divisor r_i = u_p/u_s
+    const float rowacc = row_sum4(G * (m0 * u_s * v_p));
+    G = (G - rowacc) * (u_s * __builtin_amdgcn_rcpf(u_p));
   }
   // dℓ_res = dM0 ⊙ M0 (the row-max shift contributes nothing: rows are
   // rescaled away by the first row step)
-  float dl_res[kN];
-#pragma unroll
-  for (int j = 0; j < kN; ++j) dl_res[j] = G[j] * m0[j];
-
+  const float dl_res = G * m0;
   const float dl_pre = dhp * s_pre * (1.0f - s_pre);
   const float dl_post = (tok ? dH_post[tc * kN + i] : 0.f) * 2.0f * s_post * (1.0f - s_post);
-  // dq = α·dℓ; dq·p (raw p, i.e. q/rstd) summed over the token's 24 columns
-  float dqp = a_pre * dl_pre * p_pre + a_post * dl_post * p_post;
-  float da_pre = dl_pre * q_pre, da_post = dl_post * q_post, da_res = 0.f;
-#pragma unroll
-  for (int j = 0; j < kN; ++j) {
-    dqp += a_res * dl_res[j] * p_res[j];
-    da_res += dl_res[j] * q_res[j];
-  }
-  dqp = quad_sum(dqp);
-  da_pre = quad_sum(da_pre);
-  da_post = quad_sum(da_post);
-  da_res = quad_sum(da_res);
+  // per token over its 24 columns (the pre and post columns of row i counted
+  // by the lane of column 0): dq·p with raw p (q/rstd), and the dα terms
+  const bool c0 = j == 0;
+  const float dqp = col_sum4(row_sum4(a_res * dl_res * p_res +
+                                      (c0 ? a_pre * dl_pre * p_pre + a_post * dl_post * p_post : 0.f)));
+  const float da_pre = col_sum4(row_sum4(c0 ? dl_pre * q_pre : 0.f));
+  const float da_post = col_sum4(row_sum4(c0 ? dl_post * q_post : 0.f));
+  const float da_res = col_sum4(row_sum4(dl_res * q_res));
   if (tok) {
     float* co = coef + t * kCoefStride;
-    co[i] = rstd * a_pre * dl_pre;
-    co[kN + i] = rstd * a_post * dl_post;
-#pragma unroll
-    for (int j = 0; j < kN; ++j) co[2 * kN + i * kN + j] = rstd * a_res * dl_res[j];
-    co[kC + i] = 0.f;
-    co[kC + 4 + i] = 0.f;
-    if (i == 0) co[32] = rstd * rstd * rstd * dqp / (float)K;
-    co[33 + i] = s_pre;
+    co[2 * kN + e] = rstd * a_res * dl_res;
+    if (j == 0) co[i] = rstd * a_pre * dl_pre;
+    else if (j == 1) co[kN + i] = rstd * a_post * dl_post;
+    else if (j == 2) co[33 + i] = s_pre;
+    else {
+      co[kC + i] = 0.f;
+      co[kC + 4 + i] = 0.f;
+    }
+    if (e == 0) co[32] = rstd * rstd * rstd * dqp / (float)K;
   }
-  // dbias and dα terms summed over the workgroup's 16 tokens (fixed butterfly
-  // order); tokens past T contribute zero.  One row per workgroup.
-  float red[2 * kN + 3] = {tok ? dl_pre : 0.f, tok ? dl_post : 0.f};
+  // dbias and dα terms summed over the workgroup's four tokens (fixed
+  // butterfly order); tokens past T contribute zero.  One row per workgroup.
+  float red[5] = {tok ? dl_res : 0.f, tok && j < 2 ? (j == 0 ? dl_pre : dl_post) : 0.f, tok ? da_pre : 0.f,
+                  tok ? da_post : 0.f, tok ? da_res : 0.f};
 #pragma unroll
-  for (int j = 0; j < kN; ++j) red[2 + j] = tok ? dl_res[j] : 0.f;
-  red[6] = (tok && i == 0) ? da_pre : 0.f;
-  red[7] = (tok && i == 0) ? da_post : 0.f;
-  red[8] = (tok && i == 0) ? da_res : 0.f;
+  for (int m = 16; m < 64; m <<= 1)
 #pragma unroll
-  for (int m = 4; m < 64; m <<= 1)
-#pragma unroll
-    for (int v = 0; v < 2 * kN + 3; ++v) red[v] += __shfl_xor(red[v], m, kWave);
-  if (lane < 4) {
+    for (int q = 0; q < 5; ++q) red[q] += __shfl_xor(red[q], m, kWave);
+  if (lane < 16) {
     float* dl = dlog + (int64_t)blockIdx.x * kC;
-    dl[i] = red[0];
-    dl[kN + i] = red[1];
-#pragma unroll
-    for (int j = 0; j < kN; ++j) dl[2 * kN + i * kN + j] = red[2 + j];
+    dl[2 * kN + e] = red[0];
+    if (j == 0) dl[i] = red[1];
+    else if (j == 1) dl[kN + i] = red[1];
   }
   if (lane == 0) {
-    dal[(int64_t)blockIdx.x * 4 + 0] = red[6];
-    dal[(int64_t)blockIdx.x * 4 + 1] = red[7];
-    dal[(int64_t)blockIdx.x * 4 + 2] = red[8];
+    dal[(int64_t)blockIdx.x * 4 + 0] = red[2];
+    dal[(int64_t)blockIdx.x * 4 + 1] = red[3];
+    dal[(int64_t)blockIdx.x * 4 + 2] = red[4];
     dal[(int64_t)blockIdx.x * 4 + 3] = 0.f;
   }
 }
@@ -1090,7 +1050,7 @@ __global__ __launch_bounds__(kFThreads, 1) void bwd_dx_f32_kernel(
 }
 
 // dφ = Σ_s part[s] in split order.  Workgroup 0 sums the dbias / dα rows
-// instead (one row per 16 tokens), in a fixed order.
+// instead (one row per four tokens), in a fixed order.
 __global__ __launch_bounds__(256) void dphi_bias_sum_kernel(const float* __restrict__ part,
                                                             float* __restrict__ dphi, int64_t KC, int S,
                                                             const float* __restrict__ dlog,
@@ -1108,17 +1068,28 @@ __global__ __launch_bounds__(256) void dphi_bias_sum_kernel(const float* __restr
     float acc[kV];
 #pragma unroll
     for (int c = 0; c < kV; ++c) acc[c] = 0.f;
-    for (int64_t r = t; r < R; r += 256) {
-      float4 v[kC / 4 + 1];
+    // four rows' loads in flight at once; rows past R read row r0 and add
+    // nothing, so the sums keep the row order
+    constexpr int kRows = 4;
+    for (int64_t r0 = t; r0 < R; r0 += kRows * 256) {
+      float4 v[kRows][kC / 4 + 1];
 #pragma unroll
-      for (int q = 0; q < kC / 4; ++q) v[q] = reinterpret_cast<const float4*>(dlog + r * kC)[q];
-      v[kC / 4] = reinterpret_cast<const float4*>(dal + r * 4)[0];
+      for (int u = 0; u < kRows; ++u) {
+        const int64_t r = r0 + u * 256 < R ? r0 + u * 256 : r0;
 #pragma unroll
-      for (int q = 0; q < kC / 4 + 1; ++q) {
-        const float w[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+        for (int q = 0; q < kC / 4; ++q) v[u][q] = reinterpret_cast<const float4*>(dlog + r * kC)[q];
+        v[u][kC / 4] = reinterpret_cast<const float4*>(dal + r * 4)[0];
+      }
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (4 * q + e < kV) acc[4 * q + e] += w[e];
+      for (int u = 0; u < kRows; ++u) {
+        if (r0 + u * 256 >= R) continue;
+#pragma unroll
+        for (int q = 0; q < kC / 4 + 1; ++q) {
+          const float w[4] = {v[u][q].x, v[u][q].y, v[u][q].z, v[u][q].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (4 * q + e < kV) acc[4 * q + e] += w[e];
+        }
       }
     }
 #pragma unroll
@@ -1232,7 +1203,8 @@ hipError_t launch_pre_bwd_mfma(const mhc_desc& d, const void* dh, const void* x,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t hist_bytes = (size_t)d.sinkhorn_iters * 2 * 64 * sizeof(float);
-  MHC_LAUNCH(bwd_coef_kernel, dim3((unsigned)((T + 15) / 16)), dim3(kCoefThreads), hist_bytes,
+  const int64_t coef_rows = (T + kCoefTokens - 1) / kCoefTokens;
+  MHC_LAUNCH(bwd_coef_kernel, dim3((unsigned)coef_rows), dim3(kCoefThreads), hist_bytes,
                      s, part, L.S, bias, dH_post, dH_res, coef, dlog, dal, T, d.D, d.sinkhorn_iters,
                      d.eps, d.alpha_pre, d.alpha_post, d.alpha_res, d.alpha);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1253,7 +1225,7 @@ hipError_t launch_pre_bwd_mfma(const mhc_desc& d, const void* dh, const void* x,
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t KC = (int64_t)K * kC;
   MHC_LAUNCH(dphi_bias_sum_kernel, dim3((unsigned)((KC + 255) / 256 + 1)), dim3(256), 0, s,
-                     dphi_part, dphi, KC, L.TS, dlog, dal, dbias, dalpha, (int64_t)((T + 15) / 16));
+                     dphi_part, dphi, KC, L.TS, dlog, dal, dbias, dalpha, coef_rows);
   return hipGetLastError();
 }
 
