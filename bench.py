@@ -389,6 +389,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="only the timed step, its roofline and the CPU baseline")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the fp32 configurations (so that counter runs see one workload's launches)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of one x-sized bf16 tensor (5 times), "
                          "the reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -539,7 +541,7 @@ def main():
         # the fp32 configurations of the pages' measurement paragraph
         others = {}
         for wname in ("pro_s1024_f32", "flash_s2048_f32"):
-            if wname == args.workload:
+            if wname == args.workload or args.no_other_workloads:
                 continue
             del W
             torch.cuda.empty_cache()
