@@ -33,7 +33,8 @@
  *   - Work is enqueued on `stream` and runs asynchronously; the library never
  *     allocates, frees or synchronises.  Its only global state is an atomic
  *     per-call counter (calls are thread-safe), besides the per-thread switch
- *     of mhc_trace_kernel_events.  A workspace must not be in
+ *     of mhc_trace_kernel_events and the test switch of
+ *     mhc_test_exchange_fault.  A workspace must not be in
  *     use by two calls at once.  Outputs are overwritten, except `dx` of mhc_pre_bwd,
  *     which is read-modify-write.
  *   - Errors: argument checks are synchronous and return a status without
@@ -255,6 +256,19 @@ int mhc_abi_version(void);
  * per host thread.  MHC_ERR_INVALID_ARG for a negative capacity, or a zero
  * one with events. */
 mhc_status mhc_trace_kernel_events(hipEvent_t* events, const char** names, int capacity, int* count);
+
+/* Failure injection for tests of the split-K hc_pre's bounded waits (not part
+ * of the method; off by default).  While drop_slice >= 0, workgroup
+ * `drop_slice` of every group of the split-K kernel (bf16, N = 4, D = 5120 or
+ * 2560, more tokens than the few-token path takes) publishes no exchange
+ * records, and every wait for records gives up after `spin_limit` polls.  The
+ * other members then write NaN for the tokens of every tile (h, H_pre,
+ * H_post, H_res): the failure those waits exist for, with every kernel ending
+ * normally.  drop_slice = -1 turns it off (spin_limit is then ignored).
+ * Process-wide and not synchronised: set it only while no other host thread
+ * launches mhc_pre / mhc_post_pre.  MHC_ERR_INVALID_ARG for drop_slice < -1,
+ * or for spin_limit 0 with drop_slice >= 0. */
+mhc_status mhc_test_exchange_fault(int drop_slice, unsigned spin_limit);
 
 #ifdef __cplusplus
 }

@@ -65,7 +65,7 @@ constexpr int kCG = 3;               // B column groups per step
 constexpr int kCols = 16 * kCG;      // hi[0..24) then lo[0..24)
 constexpr int kAhead = 5;            // steps whose loads are in flight
 constexpr int kHeader = 256;         // workspace bytes: ticket counter, call number
-constexpr uint32_t kSpinLimit = 1u << 20;
+constexpr uint32_t kSpinLimit = 1u << 20;  // polls of one record wait before it gives up
 // calls of the split-K hc_pre on this device so far (one copy per device)
 __device__ uint64_t g_calls = 0;
 static_assert(kSteps % kN == 0, "each step is 32 d of one stream");
@@ -240,7 +240,8 @@ __global__ __launch_bounds__(W * 64, 1) void hc_pre_tile_kernel(
     const uint16_t* __restrict__ x, const uint4* __restrict__ phip, const float* __restrict__ bias,
     uint16_t* __restrict__ h, float* __restrict__ H_pre, float* __restrict__ H_post,
     float* __restrict__ H_res, uint64_t* ctr, uint64_t* rec, int64_t T, int Q, uint32_t tag,
-    int iters, float eps, float a_pre, float a_post, float a_res, const float* __restrict__ alpha_dev) {
+    int iters, float eps, float a_pre, float a_post, float a_res, const float* __restrict__ alpha_dev,
+    uint32_t spin_limit, int drop_slice) {
   if (alpha_dev != nullptr) {  // the gate scalars are held on the device (trained α)
     a_pre = alpha_dev[0];
     a_post = alpha_dev[1];
@@ -414,7 +415,7 @@ __global__ __launch_bounds__(W * 64, 1) void hc_pre_tile_kernel(
 #pragma unroll
         for (int w = 0; w < WD; ++w) v += (va[w][0] + va[w][1]) + (va[w][2] + va[w][3]);
       }
-      if (t < rows) put(mine + u, entry(v, tag));
+      if (t < rows && slice != drop_slice) put(mine + u, entry(v, tag));
     }
 
     // gather: (a) pre[4] and the sum of squares of every token, (b) post and
@@ -444,7 +445,7 @@ __global__ __launch_bounds__(W * 64, 1) void hc_pre_tile_kernel(
             ok = ok && tagged(r[sl], tag);
           }
           if (!ok) __builtin_amdgcn_s_sleep(2);
-        } while (!ok && ++spins < kSpinLimit);
+        } while (!ok && ++spins < spin_limit);
         // a member that never published poisons the tile's values (NaN)
         v = ok ? 0.f : __builtin_nanf("");
 #pragma unroll
@@ -569,6 +570,13 @@ __global__ __launch_bounds__(W * 64, 1) void hc_pre_tile_kernel(
 
 namespace {
 
+// Failure injection for tests (mhc_test_exchange_fault): off unless set.
+struct ExchangeFault {
+  uint32_t spin_limit = tile::kSpinLimit;
+  int drop_slice = -1;
+};
+ExchangeFault g_fault;
+
 // One instantiation of the kernel: S slices, W waves, WD along d, TBW blocks.
 struct TileConfig {
   int s = 0, w = 0, wd = 0, tbw = 0;  // s = 0: not eligible
@@ -611,6 +619,11 @@ size_t phi_pack_bytes(const mhc_desc& d) {
 
 bool pre_tile_eligible(const mhc_desc& d) { return pick_tile(d).s != 0; }
 
+void set_exchange_fault(int drop_slice, uint32_t spin_limit) {
+  g_fault.drop_slice = drop_slice;
+  g_fault.spin_limit = drop_slice >= 0 ? spin_limit : tile::kSpinLimit;
+}
+
 size_t pre_tile_workspace_bytes(const mhc_desc& d) {
   const TileConfig c = pick_tile(d);
   if (c.s == 0) return 0;
@@ -638,7 +651,7 @@ hipError_t launch_pre_tile(const mhc_desc& d, const void* x, const float* phi, c
   uint16_t* hp = static_cast<uint16_t*>(h);
 #define MHC_TILE_ARGS                                                                                    \
   grid, block, 0, s, xp, phip, bias, hp, H_pre, H_post, H_res, ctr, rec, (int64_t)d.T, Q, tag, d.sinkhorn_iters, \
-      d.eps, d.alpha_pre, d.alpha_post, d.alpha_res, d.alpha
+      d.eps, d.alpha_pre, d.alpha_post, d.alpha_res, d.alpha, g_fault.spin_limit, g_fault.drop_slice
   if (c.s == 8) MHC_LAUNCH((tile::hc_pre_tile_kernel<8, 4, 4, 4>), MHC_TILE_ARGS);
   else if (c.w == 4) MHC_LAUNCH((tile::hc_pre_tile_kernel<4, 4, 4, 4>), MHC_TILE_ARGS);
   else if (c.wd == 8 && c.tbw == 2) MHC_LAUNCH((tile::hc_pre_tile_kernel<4, 8, 8, 2>), MHC_TILE_ARGS);

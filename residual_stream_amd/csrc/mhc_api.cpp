@@ -101,6 +101,12 @@ mhc_status mhc_trace_kernel_events(hipEvent_t* events, const char** names, int c
   return MHC_OK;
 }
 
+mhc_status mhc_test_exchange_fault(int drop_slice, unsigned spin_limit) {
+  if (drop_slice < -1 || (drop_slice >= 0 && spin_limit == 0)) return MHC_ERR_INVALID_ARG;
+  mhc::set_exchange_fault(drop_slice, spin_limit);
+  return MHC_OK;
+}
+
 const char* mhc_status_string(mhc_status s) {
   switch (s) {
     case MHC_OK: return "ok";

@@ -57,6 +57,10 @@ uint32_t process_tag_seed();
 // of four workgroups (bf16, N = 4, D = 5120 or 2560); φ packed into the
 // workspace as bf16 high and low parts first.
 bool pre_tile_eligible(const mhc_desc& d);
+// Test hook behind mhc_test_exchange_fault: workgroup `drop_slice` of every
+// group publishes nothing and record waits give up after spin_limit polls
+// (drop_slice = -1: off).
+void set_exchange_fault(int drop_slice, uint32_t spin_limit);
 size_t pre_tile_workspace_bytes(const mhc_desc& d);
 hipError_t launch_pre_tile(const mhc_desc& d, const void* x, const float* phi, const float* bias, void* h,
                            float* H_pre, float* H_post, float* H_res, void* ws, hipStream_t s);

@@ -42,6 +42,7 @@ ABI_FUNCTIONS = (
     "mhc_status_string",
     "mhc_abi_version",
     "mhc_trace_kernel_events",
+    "mhc_test_exchange_fault",
 )
 
 
@@ -110,6 +111,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.mhc_pre_noalloc.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.mhc_trace_kernel_events.restype = ctypes.c_int
     lib.mhc_trace_kernel_events.argtypes = [_P, _P, ctypes.c_int, _P]
+    lib.mhc_test_exchange_fault.restype = ctypes.c_int
+    lib.mhc_test_exchange_fault.argtypes = [ctypes.c_int, ctypes.c_uint]
     if path is None:
         _lib = lib
     return lib

@@ -22,6 +22,7 @@ wrong count or a column-first round moves H_res by much more than the gate.
 
 from __future__ import annotations
 
+import ctypes
 import sys
 
 import numpy as np
@@ -128,6 +129,44 @@ def test_split_k_forward_alpha1_other_group():
 def test_split_k_sinkhorn_rounds(iters, T, D):
     inp = make_inputs(T, 4, D, io="bf16", seed=iters + T + D, alpha=1.0, iters=iters, bias_std=3.0)
     check_forward(inp, tag=f"split-K rounds={iters}")
+
+
+# ------------------------------------- a group member that never publishes ---
+
+@pytest.mark.parametrize("T,D,drop", [(300, 5120, 3), (300, 2560, 0)])
+def test_lost_group_member_poisons_every_tile(T, D, drop):
+    """Forced from the host (mhc_test_exchange_fault): workgroup `drop` of
+    every group publishes no records and each record wait gives up after 64
+    polls.  Every token then comes out as NaN, a loud failure, and the kernels
+    end normally.  The next call, with the fault off, is right again: its
+    records carry a new tag, so the partial records the faulty call left in
+    the same workspace cannot match."""
+    _say(f"[fault] drop slice {drop}, T={T} D={D}")
+    lib = mhc.load()
+    inp = make_inputs(T, 4, D, io="bf16", seed=T + D + drop, alpha=1.0)
+    x, phi, bias = dev(inp.x, "bf16"), dev(inp.phi), dev(inp.bias)
+    desc = mhc.desc_for(x, inp.iters, inp.eps, inp.alphas)
+    ws = torch.empty(lib.mhc_pre_workspace_bytes(ctypes.byref(desc)), dtype=torch.uint8, device="cuda")
+    assert lib.mhc_test_exchange_fault(drop, 64) == 0
+    try:
+        bad = mhc.mhc_pre(x, phi, bias, iters=inp.iters, eps=inp.eps, alphas=inp.alphas, workspace=ws)
+        torch.cuda.synchronize()
+    finally:
+        assert lib.mhc_test_exchange_fault(-1, 0) == 0
+    for name, t in zip(("h", "H_pre", "H_post", "H_res"), bad):
+        assert torch.isnan(t.float()).all(), name
+    good = mhc.mhc_pre(x, phi, bias, iters=inp.iters, eps=inp.eps, alphas=inp.alphas, workspace=ws)
+    torch.cuda.synchronize()
+    r = oracle_forward(inp)
+    for name, t in zip(("h", "H_pre", "H_post", "H_res"), good):
+        assert_close(name, host(t), r[name], tol_of(name, "bf16"), case=f"after the fault, T={T} D={D}")
+
+
+def test_fault_switch_rejects_bad_arguments():
+    lib = mhc.load()
+    assert lib.mhc_test_exchange_fault(-2, 64) == mhc.MHC_ERR_INVALID_ARG
+    assert lib.mhc_test_exchange_fault(0, 0) == mhc.MHC_ERR_INVALID_ARG
+    assert lib.mhc_test_exchange_fault(-1, 0) == 0
 
 
 # --------------------------------- fused hc_post + next hc_pre, alpha = 1 ---
