@@ -40,9 +40,10 @@ constexpr int kSliceD = 256;          // granularity of D for this path
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+template <int POLICY = 0>
 __device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
   typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, POLICY);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 // Stores of dx, the pass's output, written once: bf16 with the non-temporal
@@ -555,7 +556,12 @@ __global__ __launch_bounds__(kDxThreads, 2) void bwd_dx_kernel(
   float4 bc[2];
   uint4 bq[2];  // MIX: an H_res row
   // raw loads only: a value computed from a load here would make the wave wait
-  // for it, and so for every load issued before it
+  // for it, and so for every load issued before it.  x, dh and dx (dx_next)
+  // are read for the last time in the step here: non-temporal loads (measured
+  // on MI355X: 102 instead of 115 µs at T = 4096, D = 5120, since the lines
+  // they would otherwise keep are the ones this pass has yet to read; the same
+  // hint on the projection pass's loads, whose x and dh this pass reads next,
+  // makes this pass slower by more than it saves there)
   auto load_tile = [&](int64_t t0, auto slot_c) {
     constexpr int SL = decltype(slot_c)::value;
     const uint32_t rows = rows_in(t0);
@@ -565,10 +571,10 @@ __global__ __launch_bounds__(kDxThreads, 2) void bwd_dx_kernel(
     const auto rh = make_rsrc(dh + tbase * D, rows * (uint32_t)D * 2);
     const auto rc = make_rsrc(coef + tbase * kCoefStride, rows * (uint32_t)kCoefStride * 4);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bx[SL][j] = ld16(rx, vo[j]);
+    for (int j = 0; j < 4; ++j) bx[SL][j] = ld16<2>(rx, vo[j]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bd[SL][j] = ld16(rd, vo[j]);
-    bh[SL] = ld16(rh, vh);
+    for (int j = 0; j < 4; ++j) bd[SL][j] = ld16<2>(rd, vo[j]);
+    bh[SL] = ld16<2>(rh, vh);
     const uint4 cv = ld16(rc, (uint32_t)((ct * kCoefStride + cc) * 4));
     bc[SL] = make_float4(__uint_as_float(cv.x), __uint_as_float(cv.y), __uint_as_float(cv.z),
                          __uint_as_float(cv.w));
