@@ -40,7 +40,12 @@ __global__ __launch_bounds__(kBwdThreads) void hc_post_bwd_generic(
 #pragma unroll
     for (int n = 0; n < N; ++n) {
       load8_stream<IO>(dxn, xb + (int64_t)n * D + d0, g[n]);
-      load8_stream<IO>(x, xb + (int64_t)n * D + d0, xv[n]);
+      // without dx, the hc_pre backward of the same block reads x next: the
+      // default policy leaves it to the caches (measured on MI355X: this
+      // kernel's time unchanged, and the hc_pre projection pass 42 instead of
+      // 50 µs when it follows directly, at T = 4096, D = 5120, bf16)
+      if constexpr (WDX) load8_stream<IO>(x, xb + (int64_t)n * D + d0, xv[n]);
+      else load8<IO>(x, xb + (int64_t)n * D + d0, xv[n]);
     }
     if constexpr (WDX) {
 #pragma unroll
