@@ -237,10 +237,10 @@ __global__ __launch_bounds__(kPackThreads) void phi_pack_tile_kernel(const float
 // W/WD along tokens, each with TBW 16-token blocks: M = 16·TBW·W/WD tokens per
 // tile.  With four waves a wave holds up to 320 registers of x (VGPRs and
 // AGPRs), so a tile can be 64 tokens and φ is read once per 64 tokens.
-template <int S, int W, int WD, int TBW>
+template <int IO, int S, int W, int WD, int TBW>
 __global__ __launch_bounds__(W * 64, 1) void hc_pre_tile_kernel(
-    const uint16_t* __restrict__ x, const uint4* __restrict__ phip, const float* __restrict__ bias,
-    uint16_t* __restrict__ h, float* __restrict__ H_pre, float* __restrict__ H_post,
+    const char* __restrict__ x, const uint4* __restrict__ phip, const float* __restrict__ bias,
+    char* __restrict__ h, float* __restrict__ H_pre, float* __restrict__ H_post,
     float* __restrict__ H_res, uint64_t* ctr, uint64_t* rec, int64_t T, int Q, uint32_t tag,
     int iters, float eps, float a_pre, float a_post, float a_res, const float* __restrict__ alpha_dev,
     uint32_t spin_limit, int drop_slice) {
@@ -256,6 +256,10 @@ __global__ __launch_bounds__(W * 64, 1) void hc_pre_tile_kernel(
   constexpr int D = kS * WD * kWaveD;
   constexpr int K = kN * D;
   static_assert(M % kS == 0 && F % 4 == 0 && F / 4 <= kWaves, "the last F/4 waves run the Sinkhorn");
+  // bytes per element of x and h, and 16-byte words of x per lane and step
+  // (fp32 keeps x in full: the collapse needs it exact)
+  constexpr int E = IO == kF32 ? 4 : 2;
+  constexpr int XW = E / 2;
 
   // φ ring of each wave (kAhead steps × 3 fragments), in the same LDS as the
   // per-wave partials [col][token] that replace it after the last step
@@ -306,20 +310,22 @@ __global__ __launch_bounds__(W * 64, 1) void hc_pre_tile_kernel(
   // into the scalar offset.
   uint32_t xvoff[TBW];
 #pragma unroll
-  for (int i = 0; i < TBW; ++i) xvoff[i] = (uint32_t)(((16 * (wt * TBW + i) + row) * K + d0 + 8 * g) * 2);
+  for (int i = 0; i < TBW; ++i) xvoff[i] = (uint32_t)(((16 * (wt * TBW + i) + row) * K + d0 + 8 * g) * E);
 
-  uint4 xr[kSteps][TBW];
+  uint4 xr[kSteps][TBW][XW];
   char* const ring_w = ring_s + wave * (kAhead * kCG * 1024);  // this wave's φ ring
   const uint32_t ring_lane = (uint32_t)(reinterpret_cast<uintptr_t>(ring_w) & 0xFFFFFFFFu) + lane * 16;
 
   auto tile_rows = [&](int64_t tl) { return (int)(T - tl * M < M ? T - tl * M : M); };
-  auto x_rsrc = [&](int64_t tl) { return make_rsrc(x + tl * M * K, (uint32_t)tile_rows(tl) * K * 2); };
+  auto x_rsrc = [&](int64_t tl) { return make_rsrc(x + tl * M * K * E, (uint32_t)tile_rows(tl) * K * E); };
   // step J's loads: x into its registers, then φ into ring slot J mod kAhead
   auto issue = [&](auto jc, __amdgpu_buffer_rsrc_t xrs) {
     constexpr int J = decltype(jc)::value;
     constexpr int n = J / kDB, jd = J % kDB;
 #pragma unroll
-    for (int i = 0; i < TBW; ++i) xr[J][i] = ld16(xrs, xvoff[i], (uint32_t)((n * D + 32 * WD * jd) * 2));
+    for (int i = 0; i < TBW; ++i)
+#pragma unroll
+      for (int w = 0; w < XW; ++w) xr[J][i][w] = ld16(xrs, xvoff[i] + 16 * w, (uint32_t)((n * D + 32 * WD * jd) * E));
 #pragma unroll
     for (int cg = 0; cg < kCG; ++cg)
       dma16(prs, ring_w + ((J % kAhead) * kCG + cg) * 1024, pvoff, (uint32_t)((J * kCG + cg) * 1024));
@@ -352,7 +358,7 @@ __global__ __launch_bounds__(W * 64, 1) void hc_pre_tile_kernel(
           // loads complete in issue order: step J's are done once no more than
           // the later steps' loads are outstanding (h stores issued between a
           // tile's first steps only make this wait longer)
-          constexpr int later = (kSteps - 1 - J < kAhead - 1 ? kSteps - 1 - J : kAhead - 1) * (TBW + kCG);
+          constexpr int later = (kSteps - 1 - J < kAhead - 1 ? kSteps - 1 - J : kAhead - 1) * (TBW * XW + kCG);
           wait_vmcnt<later>();
           u32x4_t b0, b1, b2;
           lds_read3<(J % kAhead) * kCG * 1024>(ring_lane, b0, b1, b2);
@@ -360,13 +366,34 @@ __global__ __launch_bounds__(W * 64, 1) void hc_pre_tile_kernel(
                                  make_uint4(b2.x, b2.y, b2.z, b2.w)};
 #pragma unroll
           for (int i = 0; i < TBW; ++i) {
-            const uint4 a = xr[J][i];
+            if constexpr (IO == kF32) {
+              // x = hi + lo to about 16 mantissa bits (both parts exact in
+              // bf16): hi meets every column group, lo the groups with φ's
+              // high parts (x·lo·φ_lo is below fp32 rounding)
+              float v[8];
+              const uint4 a0 = xr[J][i][0], a1 = xr[J][i][1];
+              v[0] = __uint_as_float(a0.x); v[1] = __uint_as_float(a0.y);
+              v[2] = __uint_as_float(a0.z); v[3] = __uint_as_float(a0.w);
+              v[4] = __uint_as_float(a1.x); v[5] = __uint_as_float(a1.y);
+              v[6] = __uint_as_float(a1.z); v[7] = __uint_as_float(a1.w);
+              const uint4 ahi = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                           pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+              const uint4 alo = pack_bf16x8_rest(v, ahi);
 #pragma unroll
-            for (int cg = 0; cg < kCG; ++cg) acc[i][cg] = mfma(a, bf[cg], acc[i][cg]);
-            ss[i] = dot2(a.x, ss[i]);
-            ss[i] = dot2(a.y, ss[i]);
-            ss[i] = dot2(a.z, ss[i]);
-            ss[i] = dot2(a.w, ss[i]);
+              for (int cg = 0; cg < kCG; ++cg) acc[i][cg] = mfma(ahi, bf[cg], acc[i][cg]);
+              acc[i][0] = mfma(alo, bf[0], acc[i][0]);
+              acc[i][1] = mfma(alo, bf[1], acc[i][1]);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) ss[i] = __builtin_fmaf(v[e], v[e], ss[i]);
+            } else {
+              const uint4 a = xr[J][i][0];
+#pragma unroll
+              for (int cg = 0; cg < kCG; ++cg) acc[i][cg] = mfma(a, bf[cg], acc[i][cg]);
+              ss[i] = dot2(a.x, ss[i]);
+              ss[i] = dot2(a.y, ss[i]);
+              ss[i] = dot2(a.z, ss[i]);
+              ss[i] = dot2(a.w, ss[i]);
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
           if constexpr (J + kAhead < kSteps) issue(std::integral_constant<int, J + kAhead>{}, xrs);
@@ -495,7 +522,7 @@ __global__ __launch_bounds__(W * 64, 1) void hc_pre_tile_kernel(
     const int64_t tn = tl + Q;
     const bool more = tn < ntiles;
     const __amdgpu_buffer_rsrc_t xrs_next = x_rsrc(more ? tn : tl);
-    const __amdgpu_buffer_rsrc_t hrs = make_rsrc(h + t0 * D, (uint32_t)rows * D * 2);
+    const __amdgpu_buffer_rsrc_t hrs = make_rsrc(h + t0 * D * E, (uint32_t)rows * D * E);
     // LDS reads before the first DMA of the next tile is issued (the compiler
     // waits for every pending LDS DMA before an LDS read)
     float hv[TBW][kN];
@@ -520,21 +547,41 @@ __global__ __launch_bounds__(W * 64, 1) void hc_pre_tile_kernel(
             const int t = 16 * (wt * TBW + i) + row2;
             const float* hvi = hv[i];
             float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            const uint32_t hoff = (uint32_t)((t * D + slice * (WD * kWaveD) + 32 * (JD * WD + wd) + 8 * g2) * E);
+            if constexpr (IO == kF32) {
 #pragma unroll
-            for (int n = 0; n < kN; ++n) {
-              const uint4 a = xr[n * kDB + JD][i];
-              o[0] += hvi[n] * bf16_lo(a.x);
-              o[1] += hvi[n] * bf16_hi(a.x);
-              o[2] += hvi[n] * bf16_lo(a.y);
-              o[3] += hvi[n] * bf16_hi(a.y);
-              o[4] += hvi[n] * bf16_lo(a.z);
-              o[5] += hvi[n] * bf16_hi(a.z);
-              o[6] += hvi[n] * bf16_lo(a.w);
-              o[7] += hvi[n] * bf16_hi(a.w);
+              for (int n = 0; n < kN; ++n) {
+                const uint4 a0 = xr[n * kDB + JD][i][0], a1 = xr[n * kDB + JD][i][1];
+                o[0] += hvi[n] * __uint_as_float(a0.x);
+                o[1] += hvi[n] * __uint_as_float(a0.y);
+                o[2] += hvi[n] * __uint_as_float(a0.z);
+                o[3] += hvi[n] * __uint_as_float(a0.w);
+                o[4] += hvi[n] * __uint_as_float(a1.x);
+                o[5] += hvi[n] * __uint_as_float(a1.y);
+                o[6] += hvi[n] * __uint_as_float(a1.z);
+                o[7] += hvi[n] * __uint_as_float(a1.w);
+              }
+              st16(hrs, hoff, make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
+                                         __float_as_uint(o[3])));
+              st16(hrs, hoff + 16, make_uint4(__float_as_uint(o[4]), __float_as_uint(o[5]),
+                                              __float_as_uint(o[6]), __float_as_uint(o[7])));
+            } else {
+#pragma unroll
+              for (int n = 0; n < kN; ++n) {
+                const uint4 a = xr[n * kDB + JD][i][0];
+                o[0] += hvi[n] * bf16_lo(a.x);
+                o[1] += hvi[n] * bf16_hi(a.x);
+                o[2] += hvi[n] * bf16_lo(a.y);
+                o[3] += hvi[n] * bf16_hi(a.y);
+                o[4] += hvi[n] * bf16_lo(a.z);
+                o[5] += hvi[n] * bf16_hi(a.z);
+                o[6] += hvi[n] * bf16_lo(a.w);
+                o[7] += hvi[n] * bf16_hi(a.w);
+              }
+              st16(hrs, hoff,
+                   make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                              pack_bf16x2(o[6], o[7])));
             }
-            st16(hrs, (uint32_t)((t * D + slice * (WD * kWaveD) + 32 * (JD * WD + wd) + 8 * g2) * 2),
-                 make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
-                            pack_bf16x2(o[6], o[7])));
           }
           __builtin_amdgcn_sched_barrier(0);
           if (more) issue(jc, xrs_next);
@@ -589,17 +636,23 @@ static size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 TileConfig pick_tile(const mhc_desc& d) {
   TileConfig best;
-  if (d.N != 4 || d.io != kBF16 || (d.D != 5120 && d.D != 2560)) return best;
-  static const TileConfig kCands[] = {
+  if (d.N != 4 || (d.io != kBF16 && d.io != kF32) || (d.D != 5120 && d.D != 2560)) return best;
+  static const TileConfig kBf16[] = {
       // D = 5120: 8 slices × 4 waves × 64 tokens; 4 × 8 waves × 32; 4 × 8 × 16
       {8, 4, 4, 4, 64}, {4, 8, 8, 2, 32}, {4, 8, 8, 1, 16},
       // D = 2560: 4 slices × 4 waves × 64 tokens; 4 × 8 waves (4 along d) × 32
       {4, 4, 4, 4, 64}, {4, 8, 4, 1, 32}};
+  // fp32 x takes twice the registers: 32-token tiles, 8 slices at D = 5120,
+  // 4 at D = 2560
+  static const TileConfig kF32Cands[] = {{8, 4, 4, 2, 32}, {4, 4, 4, 2, 32}};
+  const TileConfig* cands = d.io == kF32 ? kF32Cands : kBf16;
+  const int ncands = d.io == kF32 ? 2 : 5;
   const int cus = device_cu_count();
   // the one that leaves each CU the least work over the call (tiles per
   // group × tile size / slices); ties: the larger tile, which reads φ less
   int64_t best_work = -1;
-  for (const TileConfig& c : kCands) {
+  for (int ci = 0; ci < ncands; ++ci) {
+    const TileConfig& c = cands[ci];
     if (c.s * c.wd * tile::kWaveD != d.D) continue;
     const int64_t q = cus / c.s;
     if (q < 1) continue;
@@ -649,16 +702,19 @@ hipError_t launch_pre_tile(const mhc_desc& d, const void* x, const float* phi, c
   if (e != hipSuccess) return e;
   const uint32_t tag = process_tag_seed();
   const dim3 grid((unsigned)(Q * c.s)), block((unsigned)(c.w * 64));
-  const uint16_t* xp = static_cast<const uint16_t*>(x);
-  uint16_t* hp = static_cast<uint16_t*>(h);
+  const char* xp = static_cast<const char*>(x);
+  char* hp = static_cast<char*>(h);
 #define MHC_TILE_ARGS                                                                                    \
   grid, block, 0, s, xp, phip, bias, hp, H_pre, H_post, H_res, ctr, rec, (int64_t)d.T, Q, tag, d.sinkhorn_iters, \
       d.eps, d.alpha_pre, d.alpha_post, d.alpha_res, d.alpha, g_fault.spin_limit, g_fault.drop_slice
-  if (c.s == 8) MHC_LAUNCH((tile::hc_pre_tile_kernel<8, 4, 4, 4>), MHC_TILE_ARGS);
-  else if (c.w == 4) MHC_LAUNCH((tile::hc_pre_tile_kernel<4, 4, 4, 4>), MHC_TILE_ARGS);
-  else if (c.wd == 8 && c.tbw == 2) MHC_LAUNCH((tile::hc_pre_tile_kernel<4, 8, 8, 2>), MHC_TILE_ARGS);
-  else if (c.wd == 8) MHC_LAUNCH((tile::hc_pre_tile_kernel<4, 8, 8, 1>), MHC_TILE_ARGS);
-  else MHC_LAUNCH((tile::hc_pre_tile_kernel<4, 8, 4, 1>), MHC_TILE_ARGS);
+  if (d.io == kF32) {
+    if (c.s == 8) MHC_LAUNCH((tile::hc_pre_tile_kernel<kF32, 8, 4, 4, 2>), MHC_TILE_ARGS);
+    else MHC_LAUNCH((tile::hc_pre_tile_kernel<kF32, 4, 4, 4, 2>), MHC_TILE_ARGS);
+  } else if (c.s == 8) MHC_LAUNCH((tile::hc_pre_tile_kernel<kBF16, 8, 4, 4, 4>), MHC_TILE_ARGS);
+  else if (c.w == 4) MHC_LAUNCH((tile::hc_pre_tile_kernel<kBF16, 4, 4, 4, 4>), MHC_TILE_ARGS);
+  else if (c.wd == 8 && c.tbw == 2) MHC_LAUNCH((tile::hc_pre_tile_kernel<kBF16, 4, 8, 8, 2>), MHC_TILE_ARGS);
+  else if (c.wd == 8) MHC_LAUNCH((tile::hc_pre_tile_kernel<kBF16, 4, 8, 8, 1>), MHC_TILE_ARGS);
+  else MHC_LAUNCH((tile::hc_pre_tile_kernel<kBF16, 4, 8, 4, 1>), MHC_TILE_ARGS);
 #undef MHC_TILE_ARGS
   return hipGetLastError();
 }

@@ -1,9 +1,9 @@
 """The split-K hc_pre and the tiled hc_pre backward against the fp64 oracle,
 where their own structure can go wrong.
 
-The split-K forward (bf16, N = 4, D = 5120 or 2560) cuts each token's
+The split-K forward (bf16 or fp32, N = 4, D = 5120 or 2560) cuts each token's
 reduction into S slices of d (S = 8 or 4); a group of S workgroups walks the
-tiles grp, grp + Q, grp + 2Q, ... (M = 16, 32 or 64 tokens each, Q = compute
+tiles grp, grp + Q, grp + 2Q, ... (M = 16, 32 or 64 tokens each, 32 for fp32, Q = compute
 units / S), holds the tile's x on chip from the projection to the collapse,
 and workgroup `slice` of the group runs the gates and Sinkhorn of tokens
 slice·M/S .. (slice+1)·M/S − 1 of each tile.  A token's coefficients sent to
@@ -56,13 +56,16 @@ def _cus():
     return torch.cuda.get_device_properties(0).multi_processor_count
 
 
-def tile_config(T, D):
+def tile_config(T, D, io="bf16"):
     """(S, M, Q): the split-K forward's slices per group, tile size and number
     of groups for T tokens of width D, chosen as the library chooses them
-    (the candidate that leaves each compute unit the least work)."""
+    (the candidate that leaves each compute unit the least work; fp32 x takes
+    twice the registers, so its tiles are 32 tokens)."""
     cus = _cus()
     best = None
-    for s_, wd, m in ((8, 4, 64), (4, 8, 32), (4, 8, 16), (4, 4, 64), (4, 4, 32)):
+    cands = ((8, 4, 32), (4, 4, 32)) if io == "f32" else ((8, 4, 64), (4, 8, 32), (4, 8, 16), (4, 4, 64),
+                                                          (4, 4, 32))
+    for s_, wd, m in cands:
         if s_ * wd * SLICE_D_PER_WAVE != D:
             continue
         q = cus // s_
@@ -73,12 +76,12 @@ def tile_config(T, D):
     return best[1:]
 
 
-def split_k_tokens(T, D, grp=3, slice_=5, extra=24, seed=0):
+def split_k_tokens(T, D, grp=3, slice_=5, extra=24, seed=0, io="bf16"):
     """Tokens that exercise the split-K kernel's structure: all tokens of the
     first and the last tile of group `grp`, every token workgroup (grp,
     slice_) finishes in each of its tiles, the last two tokens and a random
     handful."""
-    S, M, Q = tile_config(T, D)
+    S, M, Q = tile_config(T, D, io)
     share = M // S
     ntiles = (T + M - 1) // M
     grp = min(grp, Q - 1, ntiles - 1)
@@ -111,10 +114,13 @@ def check_forward(inp, tokens=None, tag=""):
 
 # -------------------------------------------- split-K forward, alpha = 1 ---
 
-@pytest.mark.parametrize("T,D", [(4096, 5120), (4093, 5120), (2048, 2560), (4096, 2560), (4093, 2560)])
-def test_split_k_forward_alpha1_full_size(T, D):
-    inp = make_inputs(T, 4, D, io="bf16", seed=T + D, alpha=1.0)
-    check_forward(inp, tokens=split_k_tokens(T, D, seed=T), tag="split-K alpha=1")
+@pytest.mark.parametrize("T,D,io", [(4096, 5120, "bf16"), (4093, 5120, "bf16"), (2048, 2560, "bf16"),
+                                    (4096, 2560, "bf16"), (4093, 2560, "bf16"),
+                                    (1024, 5120, "f32"), (1021, 5120, "f32"), (2048, 2560, "f32"),
+                                    (2045, 2560, "f32"), (4096, 5120, "f32")])
+def test_split_k_forward_alpha1_full_size(T, D, io):
+    inp = make_inputs(T, 4, D, io=io, seed=T + D, alpha=1.0)
+    check_forward(inp, tokens=split_k_tokens(T, D, seed=T, io=io), tag="split-K alpha=1")
 
 
 def test_split_k_forward_alpha1_other_group():
@@ -125,9 +131,10 @@ def test_split_k_forward_alpha1_other_group():
 
 
 @pytest.mark.parametrize("iters", [1, 3, 64])
-@pytest.mark.parametrize("T,D", [(17, 5120), (300, 5120), (300, 2560)])
-def test_split_k_sinkhorn_rounds(iters, T, D):
-    inp = make_inputs(T, 4, D, io="bf16", seed=iters + T + D, alpha=1.0, iters=iters, bias_std=3.0)
+@pytest.mark.parametrize("T,D,io", [(17, 5120, "bf16"), (300, 5120, "bf16"), (300, 2560, "bf16"),
+                                    (17, 5120, "f32"), (300, 2560, "f32")])
+def test_split_k_sinkhorn_rounds(iters, T, D, io):
+    inp = make_inputs(T, 4, D, io=io, seed=iters + T + D, alpha=1.0, iters=iters, bias_std=3.0)
     check_forward(inp, tag=f"split-K rounds={iters}")
 
 
