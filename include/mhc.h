@@ -229,8 +229,9 @@ mhc_status mhc_post_stable_bwd(const mhc_desc* desc, const void* dx_next, const 
  * any kind.  Arguments, layouts, results (bit for bit) and errors as for
  * mhc_pre; in addition MHC_ERR_TOO_LARGE, with nothing launched, when
  * mhc_pre_workspace_bytes(desc) exceeds MHC_NOALLOC_SCRATCH_BYTES (on a
- * 256-CU MI355X every T up to 9,216 fits for bf16, N = 4, D = 5120, and up
- * to 19,712 for D = 2560; the other paths need at most 2 MB).  The first call on a
+ * 256-CU MI355X every T up to 9,216 fits for bf16, N = 4, D = 5120, up to
+ * 9,248 for fp32 at D = 5120, and up to 19,712 at D = 2560 for either; the
+ * other paths need at most 2 MB).  The first call on a
  * device looks up the buffer's device address (MHC_ERR_HIP if that fails).
  * Every call on one GPU shares that GPU's buffer, which keeps the last
  * call's contents (nothing in it needs clearing): calls on one stream are
