@@ -69,7 +69,11 @@ typedef enum mhc_status {
   MHC_ERR_TOO_LARGE = 4    /* mhc_pre_noalloc: the call needs more than MHC_NOALLOC_SCRATCH_BYTES */
 } mhc_status;
 
-/* Problem descriptor.  T = tokens (batch × sequence), N streams, D hidden size
+/* Problem descriptor.  T = tokens (batch × sequence; T = 0 is an empty batch:
+ * the token outputs are empty, nothing is launched except the zero fill of
+ * the parameter gradients that mhc_pre_bwd, mhc_pre_bwd_mix and
+ * mhc_post_stable_bwd write, whose pointers must be valid as usual; the
+ * pointers of the empty token tensors are not looked at), N streams, D hidden size
  * (multiple of 8), io = mhc_dtype, sinkhorn_iters ≥ 1 (≤ 64 for mhc_pre_bwd),
  * eps ≥ 0 inside the RMS square root, alpha_* the per-group gate scalars
  * multiplying the normalised projection before the bias is added.  `alpha`,

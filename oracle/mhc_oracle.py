@@ -99,7 +99,7 @@ def rms_rstd(x: np.ndarray, eps: float) -> np.ndarray:
     """
     x = _f64(x)
     T = x.shape[0]
-    flat = x.reshape(T, -1)
+    flat = x.reshape(T, int(np.prod(x.shape[1:])))  # explicit width: T may be 0
     return 1.0 / np.sqrt(np.mean(flat * flat, axis=1) + eps)
 
 
@@ -112,7 +112,7 @@ def project(x: np.ndarray, phi: np.ndarray, eps: float):
     x = _f64(x)
     T = x.shape[0]
     rstd = rms_rstd(x, eps)
-    raw = x.reshape(T, -1) @ _f64(phi)
+    raw = x.reshape(T, int(np.prod(x.shape[1:]))) @ _f64(phi)
     return rstd, raw, rstd[:, None] * raw
 
 

@@ -98,6 +98,19 @@ __global__ __launch_bounds__(kBwdThreads) void hc_post_bwd_generic(
   }
 }
 
+// Zero fill of n floats (the parameter gradients of an empty batch): a
+// kernel, so that a captured graph records no memset node.
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+
+hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  MHC_LAUNCH(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, (int64_t)n);
+  return hipGetLastError();
+}
+
 hipError_t launch_post_bwd(const mhc_desc& d, const void* dxn, const void* x, const void* y,
                            const float* H_post, const float* H_res, void* dx, void* dy,
                            float* dH_post, float* dH_res, hipStream_t s) {

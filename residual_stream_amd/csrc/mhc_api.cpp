@@ -54,7 +54,7 @@ bool finite(float v) { return std::isfinite(v); }
 // Shape and scalar checks common to every call.
 mhc_status check_desc(const mhc_desc* d) {
   if (d == nullptr) return MHC_ERR_INVALID_ARG;
-  if (d->T < 1 || d->T > std::numeric_limits<int32_t>::max()) return MHC_ERR_INVALID_ARG;
+  if (d->T < 0 || d->T > std::numeric_limits<int32_t>::max()) return MHC_ERR_INVALID_ARG;
   if (d->io != MHC_F32 && d->io != MHC_BF16) return MHC_ERR_INVALID_ARG;
   if (d->sinkhorn_iters < 1) return MHC_ERR_INVALID_ARG;
   if (!finite(d->eps) || d->eps < 0.f) return MHC_ERR_INVALID_ARG;
@@ -119,13 +119,25 @@ const char* mhc_status_string(mhc_status s) {
 }
 
 size_t mhc_pre_workspace_bytes(const mhc_desc* d) {
-  if (check_desc(d) != MHC_OK) return 0;
+  if (check_desc(d) != MHC_OK || d->T == 0) return 0;
   return mhc::pre_workspace_bytes(*d);
 }
 
 size_t mhc_pre_bwd_workspace_bytes(const mhc_desc* d) {
-  if (check_desc(d) != MHC_OK) return 0;
+  if (check_desc(d) != MHC_OK || d->T == 0) return 0;
   return mhc::pre_bwd_workspace_bytes(*d);
+}
+
+// An empty batch (T = 0): no token outputs, and the gradients of the
+// parameters (sums over the tokens) are zero.  Their pointers must still be
+// valid and aligned; the token tensors' pointers are not looked at.
+static mhc_status zero_params(float* const* p, const size_t* n, int count, hipStream_t stream) {
+  for (int i = 0; i < count; ++i) {
+    if (p[i] == nullptr) continue;
+    const hipError_t e = mhc::launch_fill_zero(p[i], n[i], stream);
+    if (e != hipSuccess) return from_hip(e);
+  }
+  return MHC_OK;
 }
 
 mhc_status mhc_pre(const mhc_desc* d, const void* x, const float* phi, const float* bias, void* h,
@@ -133,6 +145,7 @@ mhc_status mhc_pre(const mhc_desc* d, const void* x, const float* phi, const flo
                    size_t workspace_bytes, hipStream_t stream) {
   mhc_status st = check_desc(d);
   if (st != MHC_OK) return st;
+  if (d->T == 0) return MHC_OK;
   if (!aligned16(x) || !aligned16(phi) || !aligned16(bias) || !aligned16(h) || !aligned16(H_pre) ||
       !aligned16(H_post) || !aligned16(H_res))
     return MHC_ERR_INVALID_ARG;
@@ -147,6 +160,7 @@ mhc_status mhc_post(const mhc_desc* d, const void* x, const void* y, const float
                     const float* H_res, void* x_next, hipStream_t stream) {
   mhc_status st = check_desc(d);
   if (st != MHC_OK) return st;
+  if (d->T == 0) return MHC_OK;
   if (!aligned16(x) || !aligned16(y) || !aligned16(H_post) || !aligned16(H_res) ||
       !aligned16(x_next))
     return MHC_ERR_INVALID_ARG;
@@ -161,6 +175,7 @@ mhc_status mhc_post_bwd(const mhc_desc* d, const void* dx_next, const void* x, c
                         float* dH_post, float* dH_res, hipStream_t stream) {
   mhc_status st = check_desc(d);
   if (st != MHC_OK) return st;
+  if (d->T == 0) return MHC_OK;
   // dx may be null: the caller then forms it in mhc_pre_bwd_mix
   if (!aligned16(dx_next) || !aligned16(x) || !aligned16(y) || !aligned16(H_post) ||
       !aligned16(H_res) || (dx != nullptr && !aligned16(dx)) || !aligned16(dy) || !aligned16(dH_post) ||
@@ -183,6 +198,14 @@ mhc_status mhc_pre_bwd(const mhc_desc* d, const void* dh, const void* x, const f
   mhc_status st = check_desc(d);
   if (st != MHC_OK) return st;
   if (d->sinkhorn_iters > kMaxBwdIters) return MHC_ERR_UNSUPPORTED;
+  if (d->T == 0) {
+    if (!aligned16(dphi) || !aligned16(dbias) || (dalpha != nullptr && (reinterpret_cast<uintptr_t>(dalpha) & 3u) != 0))
+      return MHC_ERR_INVALID_ARG;
+    const size_t C = (size_t)d->N * d->N + 2 * d->N;
+    float* const p[3] = {dphi, dbias, dalpha};
+    const size_t n[3] = {(size_t)d->N * d->D * C, C, 3};
+    return zero_params(p, n, 3, stream);
+  }
   if (!aligned16(dh) || !aligned16(x) || !aligned16(phi) || !aligned16(bias) ||
       !aligned16(dH_post) || !aligned16(dH_res) || !aligned16(dx) || !aligned16(dphi) ||
       !aligned16(dbias))
@@ -204,6 +227,14 @@ mhc_status mhc_pre_bwd_mix(const mhc_desc* d, const void* dh, const void* x, con
   mhc_status st = check_desc(d);
   if (st != MHC_OK) return st;
   if (d->sinkhorn_iters > kMaxBwdIters) return MHC_ERR_UNSUPPORTED;
+  if (d->T == 0) {
+    if (!aligned16(dphi) || !aligned16(dbias) || (dalpha != nullptr && (reinterpret_cast<uintptr_t>(dalpha) & 3u) != 0))
+      return MHC_ERR_INVALID_ARG;
+    const size_t C = (size_t)d->N * d->N + 2 * d->N;
+    float* const p[3] = {dphi, dbias, dalpha};
+    const size_t n[3] = {(size_t)d->N * d->D * C, C, 3};
+    return zero_params(p, n, 3, stream);
+  }
   if (!aligned16(dh) || !aligned16(x) || !aligned16(phi) || !aligned16(bias) ||
       !aligned16(dH_post) || !aligned16(dH_res) || !aligned16(dx_next) || !aligned16(H_res) ||
       !aligned16(dx) || !aligned16(dphi) || !aligned16(dbias))
@@ -222,7 +253,7 @@ mhc_status mhc_pre_bwd_mix(const mhc_desc* d, const void* dh, const void* x, con
 }
 
 size_t mhc_post_pre_workspace_bytes(const mhc_desc* d) {
-  if (check_desc(d) != MHC_OK) return 0;
+  if (check_desc(d) != MHC_OK || d->T == 0) return 0;
   return mhc::post_pre_workspace_bytes(*d);
 }
 
@@ -232,6 +263,7 @@ mhc_status mhc_post_pre(const mhc_desc* d, const void* x, const void* y, const f
                         size_t workspace_bytes, hipStream_t stream) {
   mhc_status st = check_desc(d);
   if (st != MHC_OK) return st;
+  if (d->T == 0) return MHC_OK;
   if (!aligned16(x) || !aligned16(y) || !aligned16(H_post_in) || !aligned16(H_res_in) ||
       !aligned16(phi) || !aligned16(bias) || !aligned16(x_next) || !aligned16(h) ||
       !aligned16(H_pre) || !aligned16(H_post) || !aligned16(H_res))
@@ -251,7 +283,7 @@ mhc_status mhc_post_pre(const mhc_desc* d, const void* x, const void* y, const f
 }
 
 size_t mhc_post_stable_bwd_workspace_bytes(const mhc_desc* d, int with_y_weight, int with_out_weight) {
-  if (check_desc(d) != MHC_OK) return 0;
+  if (check_desc(d) != MHC_OK || d->T == 0) return 0;
   if (!with_y_weight && !with_out_weight) return 0;
   if (!mhc::post_stable_supported(*d)) return 0;
   return mhc::post_stable_bwd_workspace_bytes(*d, with_y_weight != 0, with_out_weight != 0);
@@ -264,6 +296,7 @@ mhc_status mhc_post_stable(const mhc_desc* d, const void* x, const void* y, cons
   if (st != MHC_OK) return st;
   if ((y_weight != nullptr || out_weight != nullptr) && !mhc::post_stable_supported(*d))
     return MHC_ERR_UNSUPPORTED;
+  if (d->T == 0) return MHC_OK;
   if (!aligned16(x) || !aligned16(y) || !aligned16(H_post) || !aligned16(H_res) || !aligned16(x_next))
     return MHC_ERR_INVALID_ARG;
   if ((y_weight != nullptr && !aligned16(y_weight)) || (out_weight != nullptr && !aligned16(out_weight)))
@@ -287,6 +320,12 @@ mhc_status mhc_post_stable_bwd(const mhc_desc* d, const void* dx_next, const voi
   const bool sw = y_weight != nullptr, pn = out_weight != nullptr;
   if ((sw || pn) && !mhc::post_stable_supported(*d)) return MHC_ERR_UNSUPPORTED;
   if (sw != (dy_weight != nullptr) || pn != (dout_weight != nullptr)) return MHC_ERR_INVALID_ARG;
+  if (d->T == 0) {
+    if ((sw && !aligned16(dy_weight)) || (pn && !aligned16(dout_weight))) return MHC_ERR_INVALID_ARG;
+    float* const p[2] = {dy_weight, dout_weight};
+    const size_t n[2] = {(size_t)d->D, (size_t)d->N * d->D};
+    return zero_params(p, n, 2, stream);
+  }
   if (!aligned16(dx_next) || !aligned16(x) || !aligned16(y) || !aligned16(H_post) ||
       !aligned16(H_res) || !aligned16(dx) || !aligned16(dy) || !aligned16(dH_post) ||
       !aligned16(dH_res))

@@ -56,6 +56,8 @@ uint32_t process_tag_seed();
 // hc_pre with whole token tiles held on chip, the reduction split over groups
 // of four workgroups (bf16, N = 4, D = 5120 or 2560); φ packed into the
 // workspace as bf16 high and low parts first.
+// n floats set to zero on the stream (a kernel, not a memset).
+hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);
 bool pre_tile_eligible(const mhc_desc& d);
 // Test hook behind mhc_test_exchange_fault: workgroup `drop_slice` of every
 // group publishes nothing and record waits give up after spin_limit polls

@@ -11,7 +11,7 @@ import torch
 from residual_stream_amd import mhc
 from residual_stream_amd.inputs import make_inputs
 
-from mhc_testlib import dev
+from mhc_testlib import dev, oracle_backward
 
 pytestmark = pytest.mark.gpu
 
@@ -87,3 +87,44 @@ def test_kernel_trace_names_and_times_each_launch():
     mhc.mhc_post(x, y, out[2], out[3])
     torch.cuda.synchronize()
     assert len(tr.durations_us()) == 3
+
+
+@pytest.mark.parametrize("io,D", [("bf16", 5120), ("f32", 256)])
+def test_empty_batch_every_call(io, D):
+    """T = 0: every call succeeds without touching the (empty) token tensors,
+    returns empty token outputs, and the parameter gradients, sums over no
+    tokens, come back as zeros (oracle: the same sums over an empty batch),
+    overwriting what the output buffers held."""
+    N, C = 4, 24
+    inp = make_inputs(0, N, D, io=io, seed=0, grads=True)
+    ref = oracle_backward(inp)
+    x, y = dev(inp.x, io), dev(inp.y, io)
+    phi, bias = dev(inp.phi), dev(inp.bias)
+    h, Hp, Hq, Hr = mhc.mhc_pre(x, phi, bias)
+    assert h.shape == (0, D) and Hp.shape == (0, N) and Hq.shape == (0, N) and Hr.shape == (0, N, N)
+    assert mhc.mhc_pre_noalloc(x, phi, bias)[0].shape == (0, D)
+    assert mhc.mhc_post(x, y, Hq, Hr).shape == (0, N, D)
+    assert mhc.mhc_post_pre(x, y, Hq, Hr, phi, bias)[0].shape == (0, N, D)
+    dxn, dh = dev(inp.dx_next, io), dev(inp.dh, io)
+    dx, dy, dHq, dHr = mhc.mhc_post_bwd(dxn, x, y, Hq, Hr)
+    assert dx.shape == (0, N, D) and dy.shape == (0, D) and dHq.shape == (0, N) and dHr.shape == (0, N, N)
+    nan = float("nan")
+    for mix in (False, True):
+        outs = (torch.full((N * D, C), nan, device="cuda"), torch.full((C,), nan, device="cuda"),
+                torch.full((4,), nan, device="cuda"))
+        if mix:
+            g = mhc.mhc_pre_bwd_mix(dh, x, phi, bias, dHq, dHr, dxn, Hr, out=(torch.empty_like(x),) + outs)
+        else:
+            g = mhc.mhc_pre_bwd(dh, x, phi, bias, dHq, dHr, dx, out=outs)
+        torch.cuda.synchronize()
+        assert g[0].shape == (0, N, D)
+        for k, t in zip(("dphi", "dbias", "dalpha"), g[1:]):
+            assert torch.equal(t.cpu().double(), torch.from_numpy(ref[k])), (mix, k)
+    if io == "bf16":
+        wy = torch.ones(D, device="cuda")
+        wx = torch.ones(N * D, device="cuda")
+        assert mhc.mhc_post_stable(x, y, Hq, Hr, y_weight=wy, out_weight=wx).shape == (0, N, D)
+        sb = mhc.mhc_post_stable_bwd(dxn, x, y, Hq, Hr, y_weight=wy, out_weight=wx)
+        torch.cuda.synchronize()
+        assert sb[0].shape == (0, N, D)
+        assert torch.count_nonzero(sb[4]) == 0 and torch.count_nonzero(sb[5]) == 0

@@ -297,3 +297,19 @@ def test_large_logit_inputs_separate_round_counts(iters):
     assert np.max(np.abs(few - ref)) / np.max(np.abs(ref)) > 0.1
     assert np.max(np.abs(few - col_first)) / np.max(np.abs(few)) > 0.1
     np.testing.assert_array_equal(few, O.hc_pre(inp.x, inp.phi, inp.bias, inp.alphas, inp.eps, iters)["H_res"])
+
+
+def test_empty_batch():
+    # no tokens: every token output is empty and the parameter gradients,
+    # sums over the tokens, are exactly zero
+    inp = make_inputs(0, 4, 64, io="f32", seed=0, grads=True)
+    pre = O.hc_pre(inp.x, inp.phi, inp.bias, inp.alphas, inp.eps, inp.iters)
+    assert pre["h"].shape == (0, 64) and pre["H_pre"].shape == (0, 4) and pre["H_res"].shape == (0, 4, 4)
+    assert O.hc_post(inp.x, inp.y, pre["H_post"], pre["H_res"]).shape == (0, 4, 64)
+    dx, dy, dHp, dHr = O.hc_post_bwd(inp.dx_next, inp.x, inp.y, pre["H_post"], pre["H_res"])
+    assert dx.shape == (0, 4, 64) and dy.shape == (0, 64)
+    g = O.hc_pre_bwd(inp.dh, inp.x, inp.phi, inp.bias, dHp, dHr, inp.alphas, inp.eps, inp.iters)
+    assert g["dx"].shape == (0, 4, 64)
+    for k in ("dphi", "dbias", "dalpha"):
+        assert np.all(g[k] == 0.0), k
+    assert g["dphi"].shape == inp.phi.shape and g["dbias"].shape == inp.bias.shape
