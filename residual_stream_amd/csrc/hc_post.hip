@@ -32,8 +32,9 @@ __global__ __launch_bounds__(kPostThreads) void hc_post_generic(
       float o[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        // fixed order, explicit fused multiply-adds (the fused hc_post +
-        // hc_pre kernel computes x_next the same way, bit for bit)
+        // fixed order, explicit fused multiply-adds: H_post·y first, then
+        // the streams in order (the order the oracle's tolerance was set for
+        // and that every caller of the write-back gets, bit for bit)
         float a = hp[n] * yv[j];
 #pragma unroll
         for (int m = 0; m < N; ++m) a = __builtin_fmaf(hr[n][m], xv[m][j], a);

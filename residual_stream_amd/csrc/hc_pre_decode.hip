@@ -179,11 +179,12 @@ __global__ __launch_bounds__(kThreads) void pre_decode_finish(
 }  // namespace decode
 
 bool pre_decode_eligible(const mhc_desc& d) {
-  // few tokens (fewer still where the split-K kernel applies: it overtakes
-  // this path between 16 and 32 tokens), and a partial-sum workspace of at
-  // most a few MB
-  const int64_t max_t = pre_tile_eligible(d) ? 16 : kDecodeMaxT;
-  return d.T <= max_t && (int64_t)d.N * d.D <= (1 << 20);
+  // few tokens, and a partial-sum workspace of at most a few MB.  Measured on
+  // MI355X at N = 4, D = 5120 (kernel time per call, bf16 and fp32): this
+  // path takes 18-26 µs from 17 to 64 tokens, the split-K kernel 28-31 µs;
+  // from 96 tokens on the split-K kernel is the faster one (this path grows
+  // by about 6 µs per 32 tokens)
+  return d.T <= kDecodeMaxT && (int64_t)d.N * d.D <= (1 << 20);
 }
 
 size_t pre_decode_workspace_bytes(const mhc_desc& d) {

@@ -68,8 +68,8 @@ def test_tiny_workload_forward_fp32():
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-@pytest.mark.parametrize("T,D", [(1, 5120), (7, 5120), (16, 5120), (17, 5120), (16, 2560), (64, 1024),
-                                 (65, 1024)])
+@pytest.mark.parametrize("T,D", [(1, 5120), (7, 5120), (16, 5120), (17, 5120), (64, 5120), (65, 5120),
+                                 (16, 2560), (64, 2560), (65, 2560), (64, 1024), (65, 1024)])
 def test_forward_few_tokens(io, T, D):
     # few-token path (k split across the chip, two launches) on both sides of
     # its token limits

@@ -40,8 +40,8 @@ def _bitwise(name, a, b):
 NAMES = ("h", "H_pre", "H_post", "H_res")
 
 # (T, D, io): largest first, then smaller inputs, crossing the kernel paths
-CALLS = [(4096, 5120, "bf16"), (300, 5120, "bf16"), (2048, 2560, "bf16"), (37, 2560, "bf16"),
-         (100, 512, "f32"), (17, 5120, "bf16")]
+CALLS = [(4096, 5120, "bf16"), (1024, 5120, "f32"), (300, 5120, "bf16"), (2048, 2560, "bf16"),
+         (37, 2560, "bf16"), (100, 512, "f32"), (17, 5120, "bf16")]
 
 
 def test_noalloc_equals_mhc_pre_call_after_call():
