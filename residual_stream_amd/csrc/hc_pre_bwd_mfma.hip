@@ -329,11 +329,12 @@ __global__ __launch_bounds__(kCoefThreads) void bwd_coef_kernel(
   const int64_t tc = tok ? t : T - 1;
   const int K = kN * D;
 
-  // slice sums (fixed order): pre i, post i, res (i, j), ss, dhp i.  Eight
-  // slices' loads in flight at once; slices past the count read slice 0 and
-  // add nothing, so the sums keep the slice order
+  // slice sums (fixed order): pre i, post i, res (i, j), ss, dhp i.  Sixteen
+  // slices' loads in flight at once (every slice of D = 5120 in one round
+  // trip); slices past the count read slice 0 and add nothing, so the sums
+  // keep the slice order
   float p_pre = 0.f, p_post = 0.f, p_res = 0.f, ss = 0.f, dhp = 0.f;
-  constexpr int kChunk = 8;
+  constexpr int kChunk = 16;
   for (int s0 = 0; s0 < nslices; s0 += kChunk) {
     float va[kChunk], vb[kChunk], vc[kChunk], vd[kChunk], ve[kChunk];
 #pragma unroll
@@ -1117,20 +1118,29 @@ __global__ __launch_bounds__(256) void dphi_bias_sum_kernel(const float* __restr
     }
     return;
   }
-  const int64_t i = (int64_t)(blockIdx.x - 1) * 256 + threadIdx.x;
+  // four consecutive entries a thread (KC is a multiple of 4), so that the
+  // whole sum fits one round of workgroups
+  const int64_t i = ((int64_t)(blockIdx.x - 1) * 256 + threadIdx.x) * 4;
   if (i >= KC) return;
-  // the splits' loads in flight together, summed in split order
-  constexpr int kChunk = 8;
-  float s = 0.f;
+  // the splits' loads in flight together (sixteen: one round trip for the
+  // usual split counts), summed in split order
+  constexpr int kChunk = 16;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j0 = 0; j0 < S; j0 += kChunk) {
-    float v[kChunk];
-#pragma unroll
-    for (int u = 0; u < kChunk; ++u) v[u] = part[(int64_t)(j0 + u < S ? j0 + u : 0) * KC + i];
+    float4 v[kChunk];
 #pragma unroll
     for (int u = 0; u < kChunk; ++u)
-      if (j0 + u < S) s += v[u];
+      v[u] = *reinterpret_cast<const float4*>(part + (int64_t)(j0 + u < S ? j0 + u : 0) * KC + i);
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u)
+      if (j0 + u < S) {
+        s.x += v[u].x;
+        s.y += v[u].y;
+        s.z += v[u].z;
+        s.w += v[u].w;
+      }
   }
-  dphi[i] = s;
+  *reinterpret_cast<float4*>(dphi + i) = s;
 }
 
 static size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
@@ -1230,7 +1240,8 @@ hipError_t launch_pre_bwd_mfma(const mhc_desc& d, const void* dh, const void* x,
                        static_cast<uint16_t*>(dx), dphi_part, T, d.D, tps, nullptr, nullptr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t KC = (int64_t)K * kC;
-  MHC_LAUNCH(dphi_bias_sum_kernel, dim3((unsigned)((KC + 255) / 256 + 1)), dim3(256), 0, s,
+  static_assert(kC % 4 == 0, "dφ rows are whole float4s");
+  MHC_LAUNCH(dphi_bias_sum_kernel, dim3((unsigned)((KC / 4 + 255) / 256 + 1)), dim3(256), 0, s,
                      dphi_part, dphi, KC, L.TS, dlog, dal, dbias, dalpha, coef_rows);
   return hipGetLastError();
 }

@@ -23,8 +23,8 @@
 //    accumulation).  A packing kernel writes both parts once per call in the
 //    B-fragment order of the matrix cores: per 32-k step three 16-column
 //    groups [hi 0..15 | hi 16..23, lo 0..7 | lo 8..23], 3 KB, which each wave
-//    streams from L2 into a ring of LDS slots with direct-to-LDS loads, nine
-//    steps ahead with four waves (five with eight), beside its x loads.
+//    streams from L2 into a ring of LDS slots with direct-to-LDS loads, five
+//    steps ahead, beside its x loads.
 //  * After the last step each workgroup sums its waves' partials in LDS (fixed
 //    order), publishes 25 numbers per token (24 raw projections and the sum
 //    of squares) as tagged 64-bit records, and gathers the other slices':
@@ -63,37 +63,12 @@ constexpr int kDB = kSteps / kN;     // 32-d blocks per stream per wave
 constexpr int kWaveD = kDB * 32;     // d per wave (160)
 constexpr int kCG = 3;               // B column groups per step
 constexpr int kCols = 16 * kCG;      // hi[0..24) then lo[0..24)
-// steps whose loads are in flight: nine with four waves (a φ ring of 27 KB a
-// wave fits in LDS), five with eight
-template <int W>
-constexpr int ahead() {
-  return W == 4 ? 9 : 5;
-}
+constexpr int kAhead = 5;            // steps whose loads are in flight
 constexpr int kHeader = 256;         // workspace bytes: ticket counter, call number
 constexpr uint32_t kSpinLimit = 1u << 20;  // polls of one record wait before it gives up
 // calls of the split-K hc_pre on this device so far (one copy per device)
 __device__ uint64_t g_calls = 0;
 static_assert(kSteps % kN == 0, "each step is 32 d of one stream");
-
-// Step processed i-th in a tile.  The first A steps interleave the d blocks of
-// streams 0 and 1 (block 0 of stream 0, block 0 of stream 1, block 1 of
-// stream 0, …): the collapse of the tile before frees the registers of d
-// block jd, so it can issue the next tile's first A steps in the order the
-// projection takes them.  The rest follow in step order.
-template <int A>
-constexpr int step_of(int i) {
-  static_assert(A <= 2 * kDB, "the ring is filled from streams 0 and 1");
-  if (i < A) return (i & 1) ? kDB + (i >> 1) : (i >> 1);
-  int k = i - A;
-  for (int J = 0; J < kSteps; ++J) {
-    const bool early = J < kDB ? J < (A + 1) / 2 : (J < 2 * kDB && J - kDB < A / 2);
-    if (!early) {
-      if (k == 0) return J;
-      --k;
-    }
-  }
-  return -1;
-}
 
 __device__ __forceinline__ f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -286,11 +261,10 @@ __global__ __launch_bounds__(W * 64, 1) void hc_pre_tile_kernel(
   constexpr int E = IO == kF32 ? 4 : 2;
   constexpr int XW = E / 2;
 
-  constexpr int kLead = ahead<W>();
-  // φ ring of each wave (kLead steps × 3 fragments), in the same LDS as the
+  // φ ring of each wave (kAhead steps × 3 fragments), in the same LDS as the
   // per-wave partials [col][token] that replace it after the last step
   // (cols 48..51: sums of squares of the four lane groups)
-  constexpr int kRingBytes = kWaves * kLead * kCG * 1024;
+  constexpr int kRingBytes = kWaves * kAhead * kCG * 1024;
   constexpr int kRedBytes = kWaves * TBW * (kCols + 4) * 16 * 4;
   __shared__ __align__(16) char ring_s[kRingBytes > kRedBytes ? kRingBytes : kRedBytes];
   float(*red)[TBW][kCols + 4][16] = reinterpret_cast<float(*)[TBW][kCols + 4][16]>(ring_s);
@@ -339,16 +313,14 @@ __global__ __launch_bounds__(W * 64, 1) void hc_pre_tile_kernel(
   for (int i = 0; i < TBW; ++i) xvoff[i] = (uint32_t)(((16 * (wt * TBW + i) + row) * K + d0 + 8 * g) * E);
 
   uint4 xr[kSteps][TBW][XW];
-  char* const ring_w = ring_s + wave * (kLead * kCG * 1024);  // this wave's φ ring
+  char* const ring_w = ring_s + wave * (kAhead * kCG * 1024);  // this wave's φ ring
   const uint32_t ring_lane = (uint32_t)(reinterpret_cast<uintptr_t>(ring_w) & 0xFFFFFFFFu) + lane * 16;
 
   auto tile_rows = [&](int64_t tl) { return (int)(T - tl * M < M ? T - tl * M : M); };
   auto x_rsrc = [&](int64_t tl) { return make_rsrc(x + tl * M * K * E, (uint32_t)tile_rows(tl) * K * E); };
-  // loads of the step processed I-th: x into its registers, then φ into ring
-  // slot I mod kLead
-  auto issue = [&](auto ic, __amdgpu_buffer_rsrc_t xrs) {
-    constexpr int I = decltype(ic)::value;
-    constexpr int J = step_of<kLead>(I);
+  // step J's loads: x into its registers, then φ into ring slot J mod kAhead
+  auto issue = [&](auto jc, __amdgpu_buffer_rsrc_t xrs) {
+    constexpr int J = decltype(jc)::value;
     constexpr int n = J / kDB, jd = J % kDB;
 #pragma unroll
     for (int i = 0; i < TBW; ++i)
@@ -356,15 +328,16 @@ __global__ __launch_bounds__(W * 64, 1) void hc_pre_tile_kernel(
       for (int w = 0; w < XW; ++w) xr[J][i][w] = ld16(xrs, xvoff[i] + 16 * w, (uint32_t)((n * D + 32 * WD * jd) * E));
 #pragma unroll
     for (int cg = 0; cg < kCG; ++cg)
-      dma16(prs, ring_w + ((I % kLead) * kCG + cg) * 1024, pvoff, (uint32_t)((J * kCG + cg) * 1024));
+      dma16(prs, ring_w + ((J % kAhead) * kCG + cg) * 1024, pvoff, (uint32_t)((J * kCG + cg) * 1024));
   };
+  static_assert(kAhead == kDB, "the collapse of d block j frees the registers of the next tile's step j");
 
   // the first tile's first steps; every later tile's are issued by the collapse
   // of the tile before it
   if (grp < ntiles) {
     const __amdgpu_buffer_rsrc_t xrs = x_rsrc(grp);
     each([&](auto jc) { issue(jc, xrs); __builtin_amdgcn_sched_barrier(0); },
-         std::make_integer_sequence<int, kLead>{});
+         std::make_integer_sequence<int, kAhead>{});
   }
   for (int64_t tl = grp; tl < ntiles; tl += Q) {
     const int64_t t0 = tl * M;
@@ -381,15 +354,14 @@ __global__ __launch_bounds__(W * 64, 1) void hc_pre_tile_kernel(
     }
     each(
         [&](auto jc) {
-          constexpr int I = decltype(jc)::value;
-          constexpr int J = step_of<kLead>(I);
+          constexpr int J = decltype(jc)::value;
           // loads complete in issue order: step J's are done once no more than
           // the later steps' loads are outstanding (h stores issued between a
           // tile's first steps only make this wait longer)
-          constexpr int later = (kSteps - 1 - I < kLead - 1 ? kSteps - 1 - I : kLead - 1) * (TBW * XW + kCG);
+          constexpr int later = (kSteps - 1 - J < kAhead - 1 ? kSteps - 1 - J : kAhead - 1) * (TBW * XW + kCG);
           wait_vmcnt<later>();
           u32x4_t b0, b1, b2;
-          lds_read3<(I % kLead) * kCG * 1024>(ring_lane, b0, b1, b2);
+          lds_read3<(J % kAhead) * kCG * 1024>(ring_lane, b0, b1, b2);
           const uint4 bf[kCG] = {make_uint4(b0.x, b0.y, b0.z, b0.w), make_uint4(b1.x, b1.y, b1.z, b1.w),
                                  make_uint4(b2.x, b2.y, b2.z, b2.w)};
 #pragma unroll
@@ -424,7 +396,7 @@ __global__ __launch_bounds__(W * 64, 1) void hc_pre_tile_kernel(
             }
           }
           __builtin_amdgcn_sched_barrier(0);
-          if constexpr (I + kLead < kSteps) issue(std::integral_constant<int, I + kLead>{}, xrs);
+          if constexpr (J + kAhead < kSteps) issue(std::integral_constant<int, J + kAhead>{}, xrs);
           __builtin_amdgcn_sched_barrier(0);
         },
         std::make_integer_sequence<int, kSteps>{});
@@ -546,8 +518,7 @@ __global__ __launch_bounds__(W * 64, 1) void hc_pre_tile_kernel(
 
     // collapse from registers, h[t][d] = Σ_n H_pre[t][n]·x[t][n][d], one d
     // block at a time; the registers of block jd then take the next tile's
-    // steps processed 2·jd-th and (2·jd + 1)-th, d block jd of streams 0 and 1
-    // (whose φ goes to the ring, free since the publish)
+    // step jd (whose φ goes to the ring, free since the publish)
     const int64_t tn = tl + Q;
     const bool more = tn < ntiles;
     const __amdgpu_buffer_rsrc_t xrs_next = x_rsrc(more ? tn : tl);
@@ -571,7 +542,6 @@ __global__ __launch_bounds__(W * 64, 1) void hc_pre_tile_kernel(
     each(
         [&](auto jc) {
           constexpr int JD = decltype(jc)::value;
-          wait_vmcnt<63 - TBW * XW>();
 #pragma unroll
           for (int i = 0; i < TBW; ++i) {
             const int t = 16 * (wt * TBW + i) + row2;
@@ -614,19 +584,7 @@ __global__ __launch_bounds__(W * 64, 1) void hc_pre_tile_kernel(
             }
           }
           __builtin_amdgcn_sched_barrier(0);
-          if (more) {
-            // at most 63 vector-memory operations outstanding (the width of
-            // the counter every wait above relies on)
-            if constexpr (2 * JD < kLead) {
-              wait_vmcnt<63 - (TBW * XW + kCG)>();
-              issue(std::integral_constant<int, 2 * JD>{}, xrs_next);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (2 * JD + 1 < kLead) {
-              wait_vmcnt<63 - (TBW * XW + kCG)>();
-              issue(std::integral_constant<int, 2 * JD + 1>{}, xrs_next);
-            }
-          }
+          if (more) issue(jc, xrs_next);
           __builtin_amdgcn_sched_barrier(0);
         },
         std::make_integer_sequence<int, kDB>{});
@@ -648,7 +606,6 @@ __global__ __launch_bounds__(W * 64, 1) void hc_pre_tile_kernel(
         c += dpp<0x128>(c);           // row_ror:8
         m *= __builtin_amdgcn_rcpf(c);
       }
-      wait_vmcnt<62>();  // room for this store within the 63 the counter holds
       if (sk_live) H_res[((t0 + slice * F + sk_u) * kN + sk_i) * kN + sk_j] = m;
     }
     // no barrier here: the next LDS writes (the partials, after the next
