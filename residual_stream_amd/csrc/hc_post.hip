@@ -6,11 +6,15 @@
 
 namespace mhc {
 
-constexpr int kPostThreads = 256;
+// At most ten waves a workgroup: a D = 5120 row in one pass, one 8-element
+// chunk a thread (measured on MI355X: 62 instead of 66 µs per call at
+// T = 4096, N = 4, D = 5120, bf16, against 256 threads and 2.5 passes).
+constexpr int kPostMaxThreads = 640;
 
-// One workgroup per token; each thread owns 8 consecutive d of every stream.
+// One workgroup per token; each thread owns 8 consecutive d of every stream
+// (d0, d0 + 8·blockDim, …).
 template <int N, int IO>
-__global__ __launch_bounds__(kPostThreads) void hc_post_generic(
+__global__ __launch_bounds__(kPostMaxThreads) void hc_post_generic(
     const void* __restrict__ x, const void* __restrict__ y, const float* __restrict__ H_post,
     const float* __restrict__ H_res, void* __restrict__ x_next, int D) {
   const int64_t t = blockIdx.x;
@@ -22,7 +26,7 @@ __global__ __launch_bounds__(kPostThreads) void hc_post_generic(
     for (int m = 0; m < N; ++m) hr[n][m] = H_res[(t * N + n) * N + m];
   }
   const int64_t xb = t * (int64_t)N * D;
-  for (int d0 = threadIdx.x * 8; d0 < D; d0 += kPostThreads * 8) {
+  for (int d0 = threadIdx.x * 8; d0 < D; d0 += (int)blockDim.x * 8) {
     float xv[N][8], yv[8];
     load8_stream<IO>(y, t * D + d0, yv);
 #pragma unroll
@@ -47,11 +51,15 @@ __global__ __launch_bounds__(kPostThreads) void hc_post_generic(
 
 hipError_t launch_post(const mhc_desc& d, const void* x, const void* y, const float* H_post,
                        const float* H_res, void* x_next, hipStream_t s) {
+  // a chunk per thread, whole waves, up to the maximum
+  const int chunks = (d.D + 7) / 8;
+  int nthr = (chunks + kWave - 1) / kWave * kWave;
+  if (nthr > kPostMaxThreads) nthr = kPostMaxThreads;
   bool ok = dispatch_n(d.N, [&](auto n_) {
     dispatch_io(d.io, [&](auto io_) {
       constexpr int N = decltype(n_)::value;
       constexpr int IO = decltype(io_)::value;
-      MHC_LAUNCH((hc_post_generic<N, IO>), dim3((unsigned)d.T), dim3(kPostThreads), 0, s,
+      MHC_LAUNCH((hc_post_generic<N, IO>), dim3((unsigned)d.T), dim3((unsigned)nthr), 0, s,
                          x, y, H_post, H_res, x_next, d.D);
     });
   });
