@@ -495,6 +495,297 @@ __global__ __launch_bounds__(kMaxThreads) void post_stable_bwd(
   }
 }
 
+// ---------------------------------------------- ten elements a thread ---
+// The backward with the post-norm, N = 4, bf16, D = 10·nthr (nthr a multiple
+// of 64, at most 512).  Its cost is vector-ALU issue, not memory: every state
+// element passes through some fifty instructions (both norms, T = 4096,
+// D = 5120: 70 M VALU instructions a call, 113 µs of SIMD time at perfect
+// balance, by the SQ counters on MI355X).  Two things of the kernel above
+// waste issue slots there: ten waves sit 3/3/2/2 on a CU's four SIMDs, so two
+// SIMDs do half as much again as the others between barriers; and with
+// ≤ 168 registers a wave it recomputes z after the second reduction and
+// unpacks x and dx_next for every use.  Here eight waves (two a SIMD, up to
+// 256 registers each) own ten elements of every row per thread, an 8-element
+// chunk at 8·i and a 2-element chunk at 8·nthr + 2·i (16- and 4-byte accesses,
+// 1 KB and 256 B runs per wave), and keep x and dx_next unpacked and z across
+// the reduction.  The loop is pipelined as far as the registers allow: the
+// next token's x and dx_next (and, without the sandwich norm, y) are loaded
+// once this token's dx pass has consumed them and arrive under the last
+// reduction and the dy pass; with the sandwich norm y runs one token further
+// ahead and the next token's Σy² rides in this token's last reduction, which
+// gives its r_y before it starts.  Arithmetic per element is the kernel
+// above's, in the same order.
+namespace e10 {
+
+constexpr int kE = 10;
+constexpr int kThreads = 512;
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t bload4(Rsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, kStream);
+}
+// 4-byte store, scalar offset 0 as for bstore16
+__device__ __forceinline__ void bstore4(Rsrc r, uint32_t voff, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)voff, 0, kStream);
+}
+
+// Ten bf16 of a row as loaded: words 0–3 the 8-element chunk, word 4 the
+// 2-element one.
+struct Row10 {
+  uint32_t w[5];
+  __device__ __forceinline__ void load(Rsrc r, uint32_t vA, uint32_t vB, uint32_t soff) {
+    const uint4 a = bload16<kStream>(r, vA, soff);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = bload4(r, vB, soff);
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < 5; ++i) w[i] = 0u;
+  }
+  __device__ __forceinline__ float operator[](int e) const {
+    return (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
+  }
+  __device__ __forceinline__ void unpack(float (&v)[kE]) const {
+#pragma unroll
+    for (int e = 0; e < kE; ++e) v[e] = (*this)[e];
+  }
+};
+
+// Ten fp32 weights: two 16-byte loads at wA and one 8-byte load at wB.
+__device__ __forceinline__ void load_w10(Rsrc r, uint32_t wA, uint32_t wB, uint32_t soff, float (&v)[kE]) {
+  const uint4 a = bload16(r, wA, soff), b = bload16(r, wA + 16, soff);
+  const u32x2_t c = __builtin_amdgcn_raw_buffer_load_b64(r, (int)wB, (int)soff, 0);
+  v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+  v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+  v[8] = __uint_as_float(c.x); v[9] = __uint_as_float(c.y);
+}
+
+// Ten values stored as bf16 (round to nearest even), stream offset `off` in
+// the lane offset.
+__device__ __forceinline__ void store10(Rsrc r, uint32_t vA, uint32_t vB, uint32_t off, const float (&v)[kE]) {
+  bstore16<kStream>(r, vA + off, make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                           pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])));
+  bstore4(r, vB + off, pack_bf16x2(v[8], v[9]));
+}
+
+// Column of element e of thread i in a row: 8·i + e, then 8·nthr + 2·i + e − 8.
+__device__ __forceinline__ int col(int e, int i, int nthr) { return e < 8 ? 8 * i + e : 8 * nthr + 2 * i + e - 8; }
+
+// Dynamic LDS: the dw_x partial sums, float2 (n, q < 5) of thread i at
+// [(n·5 + q)·nthr + i], so a wave's 8-byte accesses are contiguous.
+constexpr size_t lds_bytes(int nthr) { return (size_t)4 * 5 * nthr * sizeof(float2); }
+
+template <bool SW>
+__global__ __launch_bounds__(kThreads) void post_stable_bwd10(
+    const void* __restrict__ dxn, const void* __restrict__ x, const void* __restrict__ y,
+    const float* __restrict__ wy, const float* __restrict__ H_post, const float* __restrict__ H_res,
+    const float* __restrict__ wx, void* __restrict__ dx, void* __restrict__ dy,
+    float* __restrict__ dH_post, float* __restrict__ dH_res, float* __restrict__ part, int64_t T,
+    int D, float eps) {
+  constexpr int N = 4, E = kE;
+  // totals of the last reduction: dH_res[N²], <g_z[n], w_y⊙y or y>[N], then
+  // with the sandwich norm Σ g⊙w_y⊙y and the next token's Σ y²
+  constexpr int kS = N * N + N, kY = kS + 1;
+  constexpr int R3 = kS + (SW ? 2 : 0);
+  constexpr int kW = kThreads / kWave;
+  __shared__ float red1[kW];
+  __shared__ float red2[2][kW * 2];
+  __shared__ float red3[2][kW * R3];
+  extern __shared__ float2 accx2[];
+  const int nthr = blockDim.x, tid = threadIdx.x;
+  const int K = N * D;
+  const uint32_t rowD = (uint32_t)D * 2u;  // bytes of one bf16 stream row
+  const uint32_t vA = 16u * tid, vB = 16u * nthr + 4u * tid;  // bf16 row offsets
+  const uint32_t wA = 32u * tid, wB = 32u * nthr + 8u * tid;  // fp32 row offsets
+  float wyr[E], accy[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    wyr[e] = 0.f;
+    accy[e] = 0.f;
+  }
+  if constexpr (SW) load_w10(rsrc(wy, (uint32_t)D * 4u), wA, wB, 0, wyr);
+#pragma unroll
+  for (int q = 0; q < N * 5; ++q) accx2[q * nthr + tid] = make_float2(0.f, 0.f);
+  const Rsrc rwx = rsrc(wx, (uint32_t)K * 4u);
+
+  Row10 xr[N], dr[N], yr, y1, y2;
+  auto load_xd = [&](int64_t tt) {
+    const Rsrc rx = rsrc(static_cast<const char*>(x) + tt * K * 2, (uint32_t)K * 2u);
+    const Rsrc rd = rsrc(static_cast<const char*>(dxn) + tt * K * 2, (uint32_t)K * 2u);
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      dr[n].load(rd, vA, vB, n * rowD);
+      xr[n].load(rx, vA, vB, n * rowD);
+    }
+  };
+  auto load_y = [&](int64_t tt, Row10& yy) {
+    yy.load(rsrc(static_cast<const char*>(y) + tt * D * 2, rowD), vA, vB, 0);
+  };
+  auto sum_y2 = [&](const Row10& yy) {
+    float a = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) a += yy[e] * yy[e];
+    return a;
+  };
+  const int64_t G = gridDim.x;
+  float ry = 1.f;
+  // the grid has at most T workgroups: every one has a first token
+  load_y(blockIdx.x, yr);
+  load_xd(blockIdx.x);
+  if constexpr (SW) {
+    if (blockIdx.x + G < T) load_y(blockIdx.x + G, y1);
+    else y1.zero();
+    const float ss[1] = {sum_y2(yr)};
+    ry = __builtin_amdgcn_rsqf(lane_f(wg_sum<1>(ss, red1), 0) / (float)D + eps);
+  }
+
+  int it = 0;
+  for (int64_t t = blockIdx.x; t < T; t += G, ++it) {
+    const int p = it & 1;
+    const int64_t tn = t + G;
+    float hp[N], hr[N][N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      hp[n] = H_post[t * N + n];
+#pragma unroll
+      for (int m = 0; m < N; ++m) hr[n][m] = H_res[(t * N + n) * N + m];
+    }
+    float xf[N][E], df[N][E];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      xr[n].unpack(xf[n]);
+      dr[n].unpack(df[n]);
+    }
+    // z as in the forward (hc_post's fma order), kept for the second pass
+    float yh[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) yh[e] = SW ? (yr[e] * ry) * wyr[e] : yr[e];
+    float z[N][E];
+    float s2[2] = {0.f, 0.f};  // Σ z², Σ (w_x⊙dx_next)⊙z
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      float w[E];
+      load_w10(rwx, wA, wB, (uint32_t)(n * D) * 4u, w);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        float a = hp[n] * yh[e];
+#pragma unroll
+        for (int m = 0; m < N; ++m) a = __builtin_fmaf(hr[n][m], xf[m][e], a);
+        z[n][e] = a;
+        s2[0] += a * a;
+        s2[1] += (w[e] * df[n][e]) * a;
+      }
+    }
+    const float t2 = wg_sum<2>(s2, red2[p]);
+    const float rz = __builtin_amdgcn_rsqf(lane_f(t2, 0) / (float)K + eps);
+    const float c = rz * rz * rz * lane_f(t2, 1) / (float)K;
+    // g_z in place of z, and this token's share of dw_x
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      float w[E], a[E];
+      load_w10(rwx, wA, wB, (uint32_t)(n * D) * 4u, w);
+#pragma unroll
+      for (int q = 0; q < 5; ++q) {
+        const float2 v = accx2[(n * 5 + q) * nthr + tid];
+        a[2 * q] = v.x;
+        a[2 * q + 1] = v.y;
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float d = df[n][e], zz = z[n][e];
+        a[e] += (d * zz) * rz;
+        z[n][e] = rz * (w[e] * d) - c * zz;
+      }
+#pragma unroll
+      for (int q = 0; q < 5; ++q) accx2[(n * 5 + q) * nthr + tid] = make_float2(a[2 * q], a[2 * q + 1]);
+    }
+    // dx and the per-token sums
+    const Rsrc rdx = rsrc(static_cast<char*>(dx) + t * K * 2, (uint32_t)K * 2u);
+#pragma unroll
+    for (int m = 0; m < N; ++m) {
+      float o[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        float a = 0.f;
+#pragma unroll
+        for (int n = 0; n < N; ++n) a += hr[n][m] * z[n][e];
+        o[e] = a;
+      }
+      store10(rdx, vA, vB, m * rowD, o);
+    }
+    float g[E], acc[R3];
+#pragma unroll
+    for (int i = 0; i < R3; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float a = 0.f;
+#pragma unroll
+      for (int n = 0; n < N; ++n) a += hp[n] * z[n][e];
+      g[e] = a;
+      const float yv = yr[e];
+      const float yw = SW ? wyr[e] * yv : yv;
+#pragma unroll
+      for (int n = 0; n < N; ++n) {
+#pragma unroll
+        for (int m = 0; m < N; ++m) acc[n * N + m] += z[n][e] * xf[m][e];
+        acc[N * N + n] += z[n][e] * yw;
+      }
+      if constexpr (SW) acc[kS] += a * yw;
+    }
+    // the next token's loads, then the last reduction
+    if (tn < T) {
+      load_xd(tn);
+      if constexpr (!SW) load_y(tn, y1);
+    }
+    if constexpr (SW) {
+      if (tn + G < T) load_y(tn + G, y2);
+      else y2.zero();
+      acc[kY] = sum_y2(y1);
+    }
+    const float t3 = wg_sum<R3>(acc, red3[p]);
+    // lanes of wave 0 write the coefficient gradients of this token
+    if (tid < N * N)
+      dH_res[t * N * N + tid] = t3;
+    else if (tid < kS)
+      dH_post[t * N + tid - N * N] = SW ? ry * t3 : t3;
+    const float cy = SW ? ry * ry * ry * lane_f(t3, kS) / (float)D : 0.f;
+    float o[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if constexpr (SW) {
+        const float yv = yr[e];
+        o[e] = ry * (wyr[e] * g[e]) - cy * yv;
+        accy[e] += (g[e] * yv) * ry;
+      } else {
+        o[e] = g[e];
+      }
+    }
+    store10(rsrc(static_cast<char*>(dy) + t * D * 2, rowD), vA, vB, 0, o);
+    if constexpr (SW) {
+      ry = __builtin_amdgcn_rsqf(lane_f(t3, kY) / (float)D + eps);
+      yr = y1;
+      y1 = y2;
+    } else {
+      yr = y1;
+    }
+  }
+
+  // this workgroup's row of partial weight gradients: [dw_y (D) | dw_x (N·D)]
+  float* row = part + (int64_t)blockIdx.x * ((SW ? D : 0) + K);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int cl = col(e, tid, nthr);
+    if constexpr (SW) row[cl] = accy[e];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      const float2 v = accx2[(n * 5 + e / 2) * nthr + tid];
+      row[(SW ? D : 0) + n * D + cl] = (e & 1) ? v.y : v.x;
+    }
+  }
+}
+
+}  // namespace e10
+
 // dw[c] = Σ_{b<G} part[b][c], rows in order: 64 columns per workgroup, wave v
 // adds rows v, v + 16, … in order, then the sixteen wave sums are added in
 // wave order.  Columns [0, Dy) go to dwy, the rest to dwx.
@@ -580,20 +871,34 @@ size_t accx_lds_bytes(int N, int cpt, int nthr, bool pn) {
   return pn ? (size_t)cpt * N * 2 * nthr * sizeof(float4) : 0;
 }
 
+// The backward with ten elements a thread takes N = 4 in bf16 with the
+// post-norm on, D = 10·nthr, nthr a multiple of 64 up to 512.
+bool use_e10(const mhc_desc& d, bool pn) {
+  return pn && d.N == 4 && d.io == kBF16 && d.D % (10 * kWave) == 0 && d.D <= e10::kE * e10::kThreads;
+}
+
 // Workgroups of the backward: as many as fit on the device at once, at most
 // one per token.
 int bwd_grid(const mhc_desc& d, bool sw, bool pn) {
   Shape s;
   if (!shape_for(d.N, d.D, s)) return 0;
   int per_cu = 0;
-  dispatch(d.N, d.io, s.cpt, sw, pn, [&](auto n_, auto io_, auto c_, auto sw_, auto pn_) {
-    const void* k = reinterpret_cast<const void*>(
-        &post_stable_bwd<decltype(n_)::value, decltype(io_)::value, decltype(c_)::value,
-                         decltype(sw_)::value, decltype(pn_)::value>);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, s.nthr,
-                                                     accx_lds_bytes(d.N, s.cpt, s.nthr, pn)) != hipSuccess)
+  if (use_e10(d, pn)) {
+    const int nthr = d.D / e10::kE;
+    const void* k = sw ? reinterpret_cast<const void*>(&e10::post_stable_bwd10<true>)
+                       : reinterpret_cast<const void*>(&e10::post_stable_bwd10<false>);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, nthr, e10::lds_bytes(nthr)) != hipSuccess)
       per_cu = 1;
-  });
+  } else {
+    dispatch(d.N, d.io, s.cpt, sw, pn, [&](auto n_, auto io_, auto c_, auto sw_, auto pn_) {
+      const void* k = reinterpret_cast<const void*>(
+          &post_stable_bwd<decltype(n_)::value, decltype(io_)::value, decltype(c_)::value,
+                           decltype(sw_)::value, decltype(pn_)::value>);
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, s.nthr,
+                                                       accx_lds_bytes(d.N, s.cpt, s.nthr, pn)) != hipSuccess)
+        per_cu = 1;
+    });
+  }
   if (per_cu < 1) per_cu = 1;
   const int64_t g = (int64_t)per_cu * device_cu_count();
   return (int)(d.T < g ? d.T : g);
@@ -641,14 +946,24 @@ hipError_t launch_post_stable_bwd(const mhc_desc& d, const void* dxn, const void
   const int G = stab::bwd_grid(d, sw, pn);
   if (G < 1) return hipErrorInvalidValue;
   float* part = static_cast<float*>(ws);
-  const bool ok = stab::dispatch(d.N, d.io, sh.cpt, sw, pn, [&](auto n_, auto io_, auto c_, auto sw_, auto pn_) {
-    MHC_LAUNCH((stab::post_stable_bwd<decltype(n_)::value, decltype(io_)::value, decltype(c_)::value,
-                                              decltype(sw_)::value, decltype(pn_)::value>),
-                       dim3((unsigned)G), dim3(sh.nthr), stab::accx_lds_bytes(d.N, sh.cpt, sh.nthr, pn), s,
-                       dxn, x, y, wy, H_post, H_res, wx, dx, dy,
-                       dH_post, dH_res, part, d.T, d.D, d.eps);
-  });
-  if (!ok) return hipErrorInvalidValue;
+  if (stab::use_e10(d, pn)) {
+    const int nthr = d.D / stab::e10::kE;
+    if (sw)
+      MHC_LAUNCH(stab::e10::post_stable_bwd10<true>, dim3((unsigned)G), dim3(nthr), stab::e10::lds_bytes(nthr), s,
+                 dxn, x, y, wy, H_post, H_res, wx, dx, dy, dH_post, dH_res, part, d.T, d.D, d.eps);
+    else
+      MHC_LAUNCH(stab::e10::post_stable_bwd10<false>, dim3((unsigned)G), dim3(nthr), stab::e10::lds_bytes(nthr), s,
+                 dxn, x, y, wy, H_post, H_res, wx, dx, dy, dH_post, dH_res, part, d.T, d.D, d.eps);
+  } else {
+    const bool ok = stab::dispatch(d.N, d.io, sh.cpt, sw, pn, [&](auto n_, auto io_, auto c_, auto sw_, auto pn_) {
+      MHC_LAUNCH((stab::post_stable_bwd<decltype(n_)::value, decltype(io_)::value, decltype(c_)::value,
+                                                decltype(sw_)::value, decltype(pn_)::value>),
+                         dim3((unsigned)G), dim3(sh.nthr), stab::accx_lds_bytes(d.N, sh.cpt, sh.nthr, pn), s,
+                         dxn, x, y, wy, H_post, H_res, wx, dx, dy,
+                         dH_post, dH_res, part, d.T, d.D, d.eps);
+    });
+    if (!ok) return hipErrorInvalidValue;
+  }
   const int Dy = sw ? d.D : 0;
   const int W = Dy + (pn ? d.N * d.D : 0);
   MHC_LAUNCH(stab::stable_wsum, dim3((unsigned)((W + kWave - 1) / kWave)), dim3(stab::kSumWaves * kWave),

@@ -28,8 +28,10 @@ FLAG_IDS = ["sandwich", "postnorm", "both"]
 
 # (io, N, D, T): one chunk per thread at N = 4 (D ≤ 5120), two at N = 2,
 # four at N = 1; D = 40 and 5000 leave lanes idle; D = 8 is the smallest row
-SHAPES = [("bf16", 4, 5120, 37), ("bf16", 4, 2560, 130), ("f32", 4, 5120, 33), ("f32", 4, 40, 9),
-          ("bf16", 2, 10240, 7), ("f32", 1, 20480, 5), ("f32", 2, 5000, 11), ("bf16", 1, 8, 3)]
+# bf16 N = 4 with D a multiple of 640 (5120, 2560) takes the backward with
+# ten elements a thread when the post-norm is on; 4864 takes the general one
+SHAPES = [("bf16", 4, 5120, 37), ("bf16", 4, 2560, 130), ("bf16", 4, 4864, 21), ("f32", 4, 5120, 33),
+          ("f32", 4, 40, 9), ("bf16", 2, 10240, 7), ("f32", 1, 20480, 5), ("f32", 2, 5000, 11), ("bf16", 1, 8, 3)]
 
 
 def _say(msg):
@@ -93,11 +95,13 @@ def test_forward_and_backward_match_oracle(io, N, D, T, sw, pn):
     _check_grads(grads, _oracle_bwd(inp, Hq, Hr, wy, wx, sw, pn), tol, sw, pn)
 
 
+@pytest.mark.parametrize("T", [300, 1500])
 @pytest.mark.parametrize("sw,pn", FLAGS, ids=FLAG_IDS)
-def test_workgroups_walk_several_tokens(sw, pn):
-    # more tokens than the backward grid holds workgroups (a few per compute
-    # unit at D = 5120), so each one sums several tokens into its weight rows
-    T = 1500
+def test_workgroups_walk_several_tokens(sw, pn, T):
+    # more tokens than the backward grid holds workgroups (one per compute
+    # unit at D = 5120 with the post-norm), so each one sums several tokens
+    # into its weight rows; ragged, so that some take one token more (300:
+    # one or two tokens, so the prefetch of a token two ahead runs out early)
     _say(f"[stable] bf16 N=4 D=5120 T={T} sandwich={sw} postnorm={pn}")
     inp, Hq, Hr, wy, wx = _case("bf16", 4, 5120, T, seed=77)
     xn, grads = _gpu(inp, Hq, Hr, wy, wx, sw, pn)
