@@ -82,7 +82,7 @@ __global__ __launch_bounds__(kBwdThreads) void hc_post_bwd_generic(
   }
   if constexpr (R <= kWave) {
     // DPP wave totals and one LDS exchange; lane i of wave 0 writes total i
-    const float tot = wg_sum<R>(acc, red);
+    const float tot = wg_sum<R, kBwdThreads / kWave>(acc, red);
     if (threadIdx.x < N * N)
       dH_res[t * N * N + threadIdx.x] = tot;
     else if (threadIdx.x < R)

@@ -203,7 +203,7 @@ __global__ __launch_bounds__(kMaxThreads) void post_stable_fwd(
     for (int j = 0; j < CPT; ++j)
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss[0] += yh[j][e] * yh[j][e];
-    const float ry = __builtin_amdgcn_rsqf(lane_f(wg_sum<1>(ss, red[0]), 0) / (float)D + eps);
+    const float ry = __builtin_amdgcn_rsqf(lane_f(wg_sum<1, kMaxWaves>(ss, red[0]), 0) / (float)D + eps);
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
       float w[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kMaxThreads) void post_stable_fwd(
       for (int n = 0; n < N; ++n)
 #pragma unroll
         for (int e = 0; e < 8; ++e) ss[0] += z[j][n][e] * z[j][n][e];
-    const float rz = __builtin_amdgcn_rsqf(lane_f(wg_sum<1>(ss, red[1]), 0) / (float)K + eps);
+    const float rz = __builtin_amdgcn_rsqf(lane_f(wg_sum<1, kMaxWaves>(ss, red[1]), 0) / (float)K + eps);
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
       if (!ok[j]) continue;
@@ -344,7 +344,7 @@ __global__ __launch_bounds__(kMaxThreads) void post_stable_bwd(
         for (int j = 0; j < CPT; ++j)
 #pragma unroll
           for (int e = 0; e < 8; ++e) ss[0] += yr[j][e] * yr[j][e];
-        ry = __builtin_amdgcn_rsqf(lane_f(wg_sum<1>(ss, red1[p]), 0) / (float)D + eps);
+        ry = __builtin_amdgcn_rsqf(lane_f(wg_sum<1, kMaxWaves>(ss, red1[p]), 0) / (float)D + eps);
       }
       // z as in the forward; it is computed twice (for the two sums, then for
       // g_z) rather than kept across the reduction, which would not fit in
@@ -364,7 +364,7 @@ __global__ __launch_bounds__(kMaxThreads) void post_stable_bwd(
           }
         }
       }
-      const float t2 = wg_sum<2>(s2, red2[p]);
+      const float t2 = wg_sum<2, kMaxWaves>(s2, red2[p]);
 #pragma unroll
       for (int j = 0; j < CPT; ++j) {
         yr[j].fence();
@@ -451,7 +451,7 @@ __global__ __launch_bounds__(kMaxThreads) void post_stable_bwd(
         if constexpr (SW && !PN) acc[kY] += yv * yv;
       }
     }
-    const float t3 = wg_sum<R3>(acc, red3[p]);
+    const float t3 = wg_sum<R3, kMaxWaves>(acc, red3[p]);
     if constexpr (SW && !PN) ry = __builtin_amdgcn_rsqf(lane_f(t3, kY) / (float)D + eps);
     // lanes of wave 0 write the coefficient gradients of this token
     if (threadIdx.x < N * N)
@@ -636,7 +636,7 @@ __global__ __launch_bounds__(kThreads) void post_stable_bwd10(
     if (blockIdx.x + G < T) load_y(blockIdx.x + G, y1);
     else y1.zero();
     const float ss[1] = {sum_y2(yr)};
-    ry = __builtin_amdgcn_rsqf(lane_f(wg_sum<1>(ss, red1), 0) / (float)D + eps);
+    ry = __builtin_amdgcn_rsqf(lane_f(wg_sum<1, 0, false>(ss, red1), 0) / (float)D + eps);
   }
 
   int it = 0;
@@ -676,7 +676,7 @@ __global__ __launch_bounds__(kThreads) void post_stable_bwd10(
         s2[1] += (w[e] * df[n][e]) * a;
       }
     }
-    const float t2 = wg_sum<2>(s2, red2[p]);
+    const float t2 = wg_sum<2, 0, false>(s2, red2[p]);
     const float rz = __builtin_amdgcn_rsqf(lane_f(t2, 0) / (float)K + eps);
     const float c = rz * rz * rz * lane_f(t2, 1) / (float)K;
     // g_z in place of z, and this token's share of dw_x
@@ -742,7 +742,7 @@ __global__ __launch_bounds__(kThreads) void post_stable_bwd10(
       else y2.zero();
       acc[kY] = sum_y2(y1);
     }
-    const float t3 = wg_sum<R3>(acc, red3[p]);
+    const float t3 = wg_sum<R3, 0, false>(acc, red3[p]);
     // lanes of wave 0 write the coefficient gradients of this token
     if (tid < N * N)
       dH_res[t * N * N + tid] = t3;

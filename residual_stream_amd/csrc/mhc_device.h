@@ -174,27 +174,92 @@ __device__ __forceinline__ float wave_total63(float v) {
   return v;
 }
 
+// Wave totals of R ≤ 32 values at once, transposed: each step pairs every
+// lane with a partner whose partial sums cover other lanes, and every lane
+// keeps half of its values, adding the partner's partial of that half.  Lanes
+// l and l ^ 32 by permlane32_swap (lanes < 32 keep values i < 16), l and
+// l ^ 16 by permlane16_swap, then the partners of the single-value sum above
+// (row_mirror, row_half_mirror, quad_perm [2,3,0,1], quad_perm [1,0,3,2]).
+// Lane l ends with the wave's total of value l >> 1 (lanes l and l ^ 1
+// alike): about 70 instructions for 32 values, against ten a value one by
+// one.
+template <int R>
+__device__ __forceinline__ float wave_sums_transposed(const float (&v)[R]) {
+  static_assert(R <= 32, "two lanes a value");
+  const int lane = threadIdx.x & (kWave - 1);
+  float a[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) a[i] = i < R ? v[i] : 0.f;
+  float b[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a[i]), __float_as_uint(a[i + 16]), false, false);
+    b[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  float c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(b[i]), __float_as_uint(b[i + 8]), false, false);
+    c[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  float d[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float t0 = c[i] + dpp_f<0x140>(c[i]), t1 = c[i + 4] + dpp_f<0x140>(c[i + 4]);
+    d[i] = (lane & 8) ? t1 : t0;
+  }
+  float e[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float t0 = d[i] + dpp_f<0x141>(d[i]), t1 = d[i + 2] + dpp_f<0x141>(d[i + 2]);
+    e[i] = (lane & 4) ? t1 : t0;
+  }
+  const float t0 = e[0] + dpp_f<0x4E>(e[0]), t1 = e[1] + dpp_f<0x4E>(e[1]);
+  const float f = (lane & 2) ? t1 : t0;
+  return f + dpp_f<0xB1>(f);
+}
+
 // Sum of R ≤ 64 per-thread values over the workgroup in a fixed order (each
 // wave's total, then the waves in index order).  Returns the totals spread
 // over the lanes: lane i of every wave holds total i (i < R).  `red` holds
 // (blockDim.x / 64)·R floats.  One barrier; a caller that reduces again into
 // the same buffer alternates between two buffers, so that no wave can
-// overwrite partial sums another wave has not read yet.
-template <int R>
+// overwrite partial sums another wave has not read yet.  MAXW bounds the
+// caller's waves per workgroup, so that the waves' partial sums are read all
+// at once; MAXW = 0 reads them one by one, and TRANSPOSED = false takes the
+// wave totals one value at a time: both use fewer registers, which a kernel
+// at the register limit measured faster with (MI355X).
+template <int R, int MAXW = 1024 / kWave, bool TRANSPOSED = true>
 __device__ __forceinline__ float wg_sum(const float (&v)[R], float* red) {
   static_assert(R <= kWave, "one value per lane");
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave, nw = blockDim.x / kWave;
-  float mine = 0.f;
+  if constexpr (TRANSPOSED && R >= 8 && R <= 32) {
+    const float t = wave_sums_transposed<R>(v);
+    if (!(lane & 1) && (lane >> 1) < R) red[wave * R + (lane >> 1)] = t;
+  } else {
+    float mine = 0.f;
 #pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const float t = lane_f(wave_total63(v[i]), kWave - 1);
-    mine = lane == i ? t : mine;
+    for (int i = 0; i < R; ++i) {
+      const float t = lane_f(wave_total63(v[i]), kWave - 1);
+      mine = lane == i ? t : mine;
+    }
+    if (lane < R) red[wave * R + lane] = mine;
   }
-  if (lane < R) red[wave * R + lane] = mine;
   __syncthreads();
   float s = 0.f;
-  if (lane < R)
-    for (int w = 0; w < nw; ++w) s += red[w * R + lane];
+  if (lane < R) {
+    if constexpr (MAXW == 0) {
+      for (int w = 0; w < nw; ++w) s += red[w * R + lane];
+    } else {
+      // every load in flight at once (rows past the last wave re-read it and
+      // add nothing)
+      float p[MAXW];
+#pragma unroll
+      for (int w = 0; w < MAXW; ++w) p[w] = red[(w < nw ? w : nw - 1) * R + lane];
+#pragma unroll
+      for (int w = 0; w < MAXW; ++w) s += w < nw ? p[w] : 0.f;
+    }
+  }
   return s;
 }
 
