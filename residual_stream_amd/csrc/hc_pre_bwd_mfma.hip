@@ -1066,11 +1066,10 @@ __global__ __launch_bounds__(256) void dphi_bias_sum_kernel(const float* __restr
                                                             float* __restrict__ dalpha, int64_t R) {
   if (blockIdx.x == 0) {
     // thread t adds rows t, t + 256, … (all of a row's loads in flight at
-    // once); the per-thread sums then meet in LDS: eight partial sums of 32
-    // threads per column, then the eight in index order
+    // once); the per-thread sums then meet by wave totals and the four waves
+    // in index order
     constexpr int kV = kC + 3;
-    __shared__ float red[kV][256 + 1];
-    __shared__ float red2[kV][8];
+    __shared__ float red[(256 / kWave) * kV];
     const int t = threadIdx.x;
     float acc[kV];
 #pragma unroll
@@ -1099,23 +1098,9 @@ __global__ __launch_bounds__(256) void dphi_bias_sum_kernel(const float* __restr
         }
       }
     }
-#pragma unroll
-    for (int c = 0; c < kV; ++c) red[c][t] = acc[c];
-    __syncthreads();
-    if (t < kV * 8) {
-      const int c = t >> 3, part = t & 7;
-      float v = 0.f;
-      for (int k = 0; k < 32; ++k) v += red[c][part * 32 + k];
-      red2[c][part] = v;
-    }
-    __syncthreads();
-    if (t < kV) {
-      float v = 0.f;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) v += red2[t][k];
-      if (t < kC) dbias[t] = v;
-      else if (dalpha) dalpha[t - kC] = v;
-    }
+    const float v = wg_sum<kV, 256 / kWave>(acc, red);
+    if (t < kC) dbias[t] = v;
+    else if (t < kV && dalpha) dalpha[t - kC] = v;
     return;
   }
   // four consecutive entries a thread (KC is a multiple of 4), so that the
