@@ -95,15 +95,16 @@ def test_forward_and_backward_match_oracle(io, N, D, T, sw, pn):
     _check_grads(grads, _oracle_bwd(inp, Hq, Hr, wy, wx, sw, pn), tol, sw, pn)
 
 
-@pytest.mark.parametrize("T", [300, 1500])
+@pytest.mark.parametrize("D,T", [(5120, 300), (5120, 1500), (2560, 1100)])
 @pytest.mark.parametrize("sw,pn", FLAGS, ids=FLAG_IDS)
-def test_workgroups_walk_several_tokens(sw, pn, T):
+def test_workgroups_walk_several_tokens(sw, pn, D, T):
     # more tokens than the backward grid holds workgroups (one per compute
-    # unit at D = 5120 with the post-norm), so each one sums several tokens
-    # into its weight rows; ragged, so that some take one token more (300:
-    # one or two tokens, so the prefetch of a token two ahead runs out early)
-    _say(f"[stable] bf16 N=4 D=5120 T={T} sandwich={sw} postnorm={pn}")
-    inp, Hq, Hr, wy, wx = _case("bf16", 4, 5120, T, seed=77)
+    # unit at D = 5120 with the post-norm, two of 256 threads at D = 2560), so
+    # each one sums several tokens into its weight rows; ragged, so that some
+    # take one token more (300: one or two tokens, so the prefetch of a token
+    # two ahead runs out early)
+    _say(f"[stable] bf16 N=4 D={D} T={T} sandwich={sw} postnorm={pn}")
+    inp, Hq, Hr, wy, wx = _case("bf16", 4, D, T, seed=77)
     xn, grads = _gpu(inp, Hq, Hr, wy, wx, sw, pn)
     tol = TOL["bf16"]
     assert_close("x_next", host(xn), _oracle_fwd(inp, Hq, Hr, wy, wx, sw, pn), tol)
