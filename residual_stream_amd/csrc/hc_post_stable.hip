@@ -887,16 +887,13 @@ int bwd_grid(const mhc_desc& d, bool sw, bool pn) {
     const int nthr = d.D / e10::kE;
     const void* k = sw ? reinterpret_cast<const void*>(&e10::post_stable_bwd10<true>)
                        : reinterpret_cast<const void*>(&e10::post_stable_bwd10<false>);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, nthr, e10::lds_bytes(nthr)) != hipSuccess)
-      per_cu = 1;
+    per_cu = occupancy_per_cu(k, nthr, e10::lds_bytes(nthr));
   } else {
     dispatch(d.N, d.io, s.cpt, sw, pn, [&](auto n_, auto io_, auto c_, auto sw_, auto pn_) {
       const void* k = reinterpret_cast<const void*>(
           &post_stable_bwd<decltype(n_)::value, decltype(io_)::value, decltype(c_)::value,
                            decltype(sw_)::value, decltype(pn_)::value>);
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, s.nthr,
-                                                       accx_lds_bytes(d.N, s.cpt, s.nthr, pn)) != hipSuccess)
-        per_cu = 1;
+      per_cu = occupancy_per_cu(k, s.nthr, accx_lds_bytes(d.N, s.cpt, s.nthr, pn));
     });
   }
   if (per_cu < 1) per_cu = 1;

@@ -7,6 +7,7 @@
 #include <chrono>
 #include <cmath>
 #include <limits>
+#include <mutex>
 
 #include "mhc.h"
 #include "mhc_internal.h"
@@ -25,6 +26,36 @@ int device_cu_count() {
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
     n = 256;
   if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Resident workgroups per CU of a kernel at a block size and dynamic LDS, from
+// the runtime's occupancy query, kept per device in a fixed table (the query
+// otherwise costs host time on every call); at least 1.
+int occupancy_per_cu(const void* kernel, int threads, size_t lds) {
+  struct Entry {
+    int dev;
+    const void* kernel;
+    int threads;
+    size_t lds;
+    int per_cu;
+  };
+  constexpr int kSlots = 64;
+  static Entry table[kSlots];
+  static int used = 0;
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; ++i)
+      if (table[i].dev == dev && table[i].kernel == kernel && table[i].threads == threads && table[i].lds == lds)
+        return table[i].per_cu;
+  }
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, lds) != hipSuccess || n < 1) n = 1;
+  std::lock_guard<std::mutex> lock(mu);
+  if (used < kSlots) table[used++] = Entry{dev, kernel, threads, lds, n};
   return n;
 }
 

@@ -48,6 +48,7 @@ inline void trace_after(hipStream_t s, const char* name) {
 // Compute units of the current device (cached per device; a property query,
 // not mutable state).
 int device_cu_count();
+int occupancy_per_cu(const void* kernel, int threads, size_t lds);
 
 // Seed of the exchange-record tags of the split-K hc_pre, drawn once per
 // process (each call adds a per-device call number on the device).
