@@ -12,8 +12,9 @@ namespace mhc {
 constexpr int kPostMaxThreads = 640;
 
 // One workgroup per token; each thread owns 8 consecutive d of every stream
-// (d0, d0 + 8·blockDim, …).
-template <int N, int IO>
+// (d0, d0 + 8·blockDim, …).  x_next is stored non-temporally, unless KEEP:
+// then with the default policy, for a kernel that reads it right after.
+template <int N, int IO, bool KEEP>
 __global__ __launch_bounds__(kPostMaxThreads) void hc_post_generic(
     const void* __restrict__ x, const void* __restrict__ y, const float* __restrict__ H_post,
     const float* __restrict__ H_res, void* __restrict__ x_next, int D) {
@@ -44,13 +45,16 @@ __global__ __launch_bounds__(kPostMaxThreads) void hc_post_generic(
         for (int m = 0; m < N; ++m) a = __builtin_fmaf(hr[n][m], xv[m][j], a);
         o[j] = a;
       }
-      store8_stream<IO>(x_next, xb + (int64_t)n * D + d0, o);
+      if constexpr (KEEP)
+        store8<IO>(x_next, xb + (int64_t)n * D + d0, o);
+      else
+        store8_stream<IO>(x_next, xb + (int64_t)n * D + d0, o);
     }
   }
 }
 
 hipError_t launch_post(const mhc_desc& d, const void* x, const void* y, const float* H_post,
-                       const float* H_res, void* x_next, hipStream_t s) {
+                       const float* H_res, void* x_next, hipStream_t s, bool keep_out) {
   // a chunk per thread, whole waves, up to the maximum
   const int chunks = (d.D + 7) / 8;
   int nthr = (chunks + kWave - 1) / kWave * kWave;
@@ -59,8 +63,12 @@ hipError_t launch_post(const mhc_desc& d, const void* x, const void* y, const fl
     dispatch_io(d.io, [&](auto io_) {
       constexpr int N = decltype(n_)::value;
       constexpr int IO = decltype(io_)::value;
-      MHC_LAUNCH((hc_post_generic<N, IO>), dim3((unsigned)d.T), dim3((unsigned)nthr), 0, s,
-                         x, y, H_post, H_res, x_next, d.D);
+      if (keep_out)
+        MHC_LAUNCH((hc_post_generic<N, IO, true>), dim3((unsigned)d.T), dim3((unsigned)nthr), 0, s,
+                   x, y, H_post, H_res, x_next, d.D);
+      else
+        MHC_LAUNCH((hc_post_generic<N, IO, false>), dim3((unsigned)d.T), dim3((unsigned)nthr), 0, s,
+                   x, y, H_post, H_res, x_next, d.D);
     });
   });
   if (!ok) return hipErrorInvalidValue;

@@ -525,7 +525,8 @@ hipError_t launch_pre(const mhc_desc& d, const void* x, const float* phi, const 
 hipError_t launch_post_pre(const mhc_desc& d, const void* x, const void* y, const float* H_post_in,
                            const float* H_res_in, void* x_next, const float* phi, const float* bias,
                            void* h, float* H_pre, float* H_post, float* H_res, void* ws, hipStream_t s) {
-  const hipError_t e = launch_post(d, x, y, H_post_in, H_res_in, x_next, s);
+  // x_next keeps the default cache policy here: hc_pre reads it next
+  const hipError_t e = launch_post(d, x, y, H_post_in, H_res_in, x_next, s, true);
   if (e != hipSuccess) return e;
   return launch_pre(d, x_next, phi, bias, h, H_pre, H_post, H_res, ws, s);
 }

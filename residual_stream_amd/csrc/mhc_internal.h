@@ -87,7 +87,8 @@ hipError_t launch_post_pre(const mhc_desc& d, const void* x, const void* y, cons
                            const float* H_res_in, void* x_next, const float* phi, const float* bias,
                            void* h, float* H_pre, float* H_post, float* H_res, void* ws, hipStream_t s);
 hipError_t launch_post(const mhc_desc& d, const void* x, const void* y, const float* H_post,
-                       const float* H_res, void* x_next, hipStream_t s);
+                       const float* H_res, void* x_next, hipStream_t s,
+                       bool keep_out = false);
 
 hipError_t launch_post_bwd(const mhc_desc& d, const void* dxn, const void* x, const void* y,
                            const float* H_post, const float* H_res, void* dx, void* dy,
