@@ -70,7 +70,8 @@ constexpr int kCG = 3;               // B column groups per step
 constexpr int kCols = 16 * kCG;      // hi[0..24) then lo[0..24)
 constexpr int kAhead = 5;            // steps whose loads are in flight
 constexpr int kCounters = 8;         // ticket counters at most, one per 256 bytes
-// workspace bytes: ticket counter c at byte 256·c, the call number at byte 8
+// workspace bytes: ticket counter c at byte 256·c, a copy of the call number
+// at byte 256·c + 8
 constexpr int kHeader = 256 * kCounters;
 constexpr uint32_t kSpinLimit = 1u << 20;  // polls of one record wait before it gives up
 // calls of the split-K hc_pre on this device so far (one copy per device)
@@ -186,10 +187,14 @@ __global__ __launch_bounds__(kPackThreads) void phi_pack_tile_kernel(const float
   // every call takes a number of its own from the device-wide counter, before
   // the main kernel starts, and leaves it in its workspace header: the main
   // kernel tags its records with it (also on every replay of a HIP graph)
-  if (blockIdx.x == 0 && threadIdx.x == 0)
-    __hip_atomic_store(call_no, __hip_atomic_fetch_add(&g_calls, (uint64_t)1, __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT) + 1,
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // (one copy beside each slice's ticket counter, so that the main kernel's
+  // workgroups read it from S addresses rather than one)
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    const uint64_t v = __hip_atomic_fetch_add(&g_calls, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+#pragma unroll
+    for (int c = 0; c < kCounters; ++c)
+      __hip_atomic_store(call_no + 32 * c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   __shared__ float rows_s[kPackItems][32 * kC];
   static_assert(32 * kC == 4 * kPackThreads, "one float4 per thread and item");
   const int nitems = D / kWaveD * kSteps;
@@ -294,7 +299,8 @@ __global__ __launch_bounds__(W * 64, 1) void hc_pre_tile_kernel(
                         (uint64_t)Q);
     ticket_s = g * kS + sl;
     // process seed + this call's number
-    tag_s = (tag + (uint32_t)__hip_atomic_load(ctr + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) | 0x80000000u;
+    tag_s = (tag + (uint32_t)__hip_atomic_load(ctr + 32 * sl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) |
+            0x80000000u;
   }
   if (threadIdx.x < kC) bias_s[threadIdx.x] = bias[threadIdx.x];
   __syncthreads();
