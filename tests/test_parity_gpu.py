@@ -177,6 +177,34 @@ def test_deterministic_and_side_stream():
         assert torch.equal(b[k], b2[k]), k
 
 
+def test_split_k_workspace_shared_across_configurations():
+    # one workspace, never cleared, shared by calls of different tile
+    # configurations (8 or 4 slices, bf16 or fp32, ragged T): the ticket
+    # counters and exchange records it keeps from the calls before must not
+    # change any result, bit for bit against a fresh zeroed workspace
+    cases = [(4096, 5120, "bf16"), (300, 2560, "bf16"), (1024, 5120, "f32"), (4093, 5120, "bf16")]
+    io_of = {"bf16": mhc.MHC_BF16, "f32": mhc.MHC_F32}
+    need = max(mhc.workspace_bytes("pre", T, 4, D, io_of[io]) for T, D, io in cases)
+    shared = torch.empty(need, dtype=torch.uint8, device="cuda")
+    shared.fill_(0x5A)
+    runs = []
+    for i, (T, D, io) in enumerate(cases):
+        _say(f"[ws] T={T} D={D} io={io}")
+        inp = make_inputs(T, 4, D, io=io, seed=40 + i, alpha=1.0)
+        args = (dev(inp.x, io), dev(inp.phi), dev(inp.bias))
+        kw = dict(iters=inp.iters, eps=inp.eps, alphas=inp.alphas)
+        fresh = torch.zeros(need, dtype=torch.uint8, device="cuda")
+        ref = mhc.mhc_pre(*args, workspace=fresh, **kw)
+        runs.append((args, kw, ref))
+    torch.cuda.synchronize()
+    for rnd in range(2):
+        for (args, kw, ref), (T, D, io) in zip(runs, cases):
+            got = mhc.mhc_pre(*args, workspace=shared, **kw)
+            torch.cuda.synchronize()
+            for name, a, b in zip(("h", "H_pre", "H_post", "H_res"), got, ref):
+                assert torch.equal(a, b), (rnd, T, D, io, name)
+
+
 def test_workspace_too_small_rejected():
     inp = make_inputs(8, 4, 64, io="f32", seed=1, grads=True)
     x = dev(inp.x, "f32")
