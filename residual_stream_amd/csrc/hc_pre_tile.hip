@@ -294,13 +294,19 @@ __global__ __launch_bounds__(W * 64, 1) void hc_pre_tile_kernel(
     // are each taken once, whatever the counters held
     static_assert(kS <= kCounters, "a counter per slice");
     const int sl = (int)blockIdx.x % kS;
-    const int g = (int)(__hip_atomic_fetch_add(ctr + 32 * sl, (uint64_t)1, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT) %
-                        (uint64_t)Q);
-    ticket_s = g * kS + sl;
-    // process seed + this call's number
-    tag_s = (tag + (uint32_t)__hip_atomic_load(ctr + 32 * sl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) |
-            0x80000000u;
+    const uint64_t v = __hip_atomic_fetch_add(ctr + 32 * sl, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // v mod Q in 32-bit arithmetic: (hi·2³² + lo) mod q, with 2³² mod q =
+    // ((2³² − 1) mod q + 1) mod q (products stay below q² < 2³²: Q is at
+    // most the CU count)
+    const uint32_t q = (uint32_t)Q, hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
+    const uint32_t p32 = (0xFFFFFFFFu % q + 1u) % q;
+    ticket_s = (int)(((hi % q) * p32 + lo % q) % q) * kS + sl;
+  } else if (threadIdx.x == kWave) {
+    // process seed + this call's number, read by another wave so that its
+    // round trip overlaps the ticket's
+    const uint64_t cn =
+        __hip_atomic_load(ctr + 32 * ((int)blockIdx.x % kS) + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    tag_s = (tag + (uint32_t)cn) | 0x80000000u;
   }
   if (threadIdx.x < kC) bias_s[threadIdx.x] = bias[threadIdx.x];
   __syncthreads();
